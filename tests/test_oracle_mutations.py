@@ -1,0 +1,106 @@
+"""Plant plausible mistakes in the oracle (CPU only) and check a pin catches each.
+
+Every mutation replaces one oracle function with a subtly wrong version for
+the duration of one test; the listed pin tests must then fail.  This is what
+makes the pins in test_oracle_pins.py worth trusting.
+"""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import moe_oracle as O
+import tests.test_oracle_pins as pins
+
+_orig = {name: getattr(O, name) for name in
+         ["router_logits", "gumbel_noise", "topk_by_keys", "gate_weights", "capacity",
+          "permute", "swiglu_ffn", "combine", "fp8_e4m3fn_decode", "selection_keys",
+          "silu"]}
+
+
+def m_router_wrong_column(x, w):
+    return _orig["router_logits"](x, np.asarray(w)[:, ::-1])
+
+
+def m_gumbel_sign(u):
+    return (np.log(-np.log(np.asarray(u, np.float64)))).astype(np.float32)
+
+
+def m_topk_ties_high(keys, k):
+    keys = np.asarray(keys, np.float32)
+    rev = keys[:, ::-1]
+    idx, gs, go = _orig["topk_by_keys"](rev, k)
+    return (keys.shape[1] - 1 - idx).astype(np.int32), gs, go
+
+
+def m_weights_no_renorm(basis, idx, rc):
+    rc2 = O.RouteConfig(rc.E, rc.k, rc.score, 0, rc.tau, rc.bias_mode)
+    return _orig["gate_weights"](basis, idx, rc2)
+
+
+def m_capacity_ceil(T, k, E, cf):
+    if cf <= 0:
+        return None
+    return max(1, int(math.ceil(T * k * cf / E)))
+
+
+def m_capacity_no_floor1(T, k, E, cf):
+    if cf <= 0:
+        return None
+    return int(math.floor(T * k * cf / E))
+
+
+def m_permute_keep_one_extra(idx, E, C):
+    return _orig["permute"](idx, E, None if C is None else C + 1)
+
+
+def m_swiglu_swapped(rows, wg, wu, wd):
+    return _orig["swiglu_ffn"](rows, wu, wg, wd)
+
+
+def m_swiglu_no_silu(rows, wg, wu, wd):
+    r = np.asarray(rows, np.float64)
+    return ((r @ wg.T) * (r @ wu.T)) @ wd.T
+
+
+def m_combine_unweighted(y, dest, w, sh=None):
+    return _orig["combine"](y, dest, np.ones_like(w), sh)
+
+
+def m_fp8_bias8(codes):
+    return _orig["fp8_e4m3fn_decode"](codes) / 2.0
+
+
+def m_bias_in_weights(z, rc, bias=None, u=None):
+    key, basis = _orig["selection_keys"](z, rc, bias, u)
+    if rc.bias_mode == O.BIAS_SELECT_ONLY and rc.score == O.SCORE_SIGMOID:
+        basis = key
+    return key, basis
+
+
+MUTATIONS = [
+    ("router_logits", m_router_wrong_column, ["test_router_unit_vectors_select_rows"]),
+    ("gumbel_noise", m_gumbel_sign, ["test_gumbel_statistics_match_gumbel01",
+                                     "test_gumbel_noise_closed_form_points"]),
+    ("topk_by_keys", m_topk_ties_high, ["test_topk_bruteforce_with_ties"]),
+    ("gate_weights", m_weights_no_renorm, ["test_softmax_then_topk_equals_topk_then_softmax"]),
+    ("capacity", m_capacity_ceil, ["test_capacity_worked_examples_from_pages"]),
+    ("capacity", m_capacity_no_floor1, ["test_capacity_worked_examples_from_pages"]),
+    ("permute", m_permute_keep_one_extra, ["test_forced_overflow_closed_form"]),
+    ("swiglu_ffn", m_swiglu_swapped, ["test_single_expert_top1_is_dense_ffn"]),
+    ("swiglu_ffn", m_swiglu_no_silu, ["test_single_expert_top1_is_dense_ffn",
+                                      "test_swiglu_bruteforce_tiny"]),
+    ("combine", m_combine_unweighted, ["test_identity_expert_combine_inverts_permute"]),
+    ("fp8_e4m3fn_decode", m_fp8_bias8, ["test_fp8_decode_all_codes"]),
+    ("selection_keys", m_bias_in_weights, ["test_selection_only_bias_steers_but_does_not_weigh"]),
+]
+
+
+@pytest.mark.parametrize("target,mutant,catchers", MUTATIONS,
+                         ids=[m[1].__name__ for m in MUTATIONS])
+def test_mutation_is_caught(monkeypatch, target, mutant, catchers):
+    monkeypatch.setattr(O, target, mutant)
+    for name in catchers:
+        fn = getattr(pins, name)
+        with pytest.raises(AssertionError):
+            fn()

@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against things other than itself (CPU only).
+
+Each test checks one part of the oracle against a closed form, an invariant,
+a special case that reduces to a library routine, brute force on a tiny
+input, or a number the pages print (tests/golden/).  test_oracle_mutations.py
+shows that plausible mistakes planted in the oracle fail at least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rng(seed=0):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------- S1 router
+def test_router_logits_match_exact_sum_bruteforce():
+    """z = fl32(exact dot): math.fsum of exact float64 products (brute force)."""
+    r = _rng(1)
+    x = r.standard_normal((5, 37)).astype(np.float32)
+    w = (0.02 * r.standard_normal((37, 3))).astype(np.float32)
+    z = O.router_logits(x, w)
+    for t in range(5):
+        for e in range(3):
+            exact = math.fsum(float(x[t, i]) * float(w[i, e]) for i in range(37))
+            ref = np.float32(exact)
+            # the float64 matmul may double-round: at most one float32 ulp away
+            assert abs(float(z[t, e]) - float(ref)) <= float(np.spacing(np.float32(abs(ref))))
+
+
+def test_router_unit_vectors_select_rows():
+    """Closed form: x = e_i gives z = W_r[i, :] exactly; E = 1 gives a column dot."""
+    r = _rng(2)
+    w = r.standard_normal((6, 4)).astype(np.float32)
+    z = O.router_logits(np.eye(6, dtype=np.float32), w)
+    assert np.array_equal(z, w)
+    w1 = r.standard_normal((6, 1)).astype(np.float32)
+    x = r.standard_normal((3, 6)).astype(np.float32)
+    z1 = O.router_logits(x, w1)
+    assert z1.shape == (3, 1)
+
+
+# ---------------------------------------------------------------- S2 top-k
+def test_topk_bruteforce_with_ties():
+    """Top-k equals Python's sort by (-key, expert); ties go to the lower index."""
+    r = _rng(3)
+    keys = r.integers(-3, 4, size=(200, 7)).astype(np.float32)  # many exact ties
+    for k in (1, 2, 3, 7):
+        idx, gs, go = O.topk_by_keys(keys, k)
+        for t in range(200):
+            ref = sorted(range(7), key=lambda e: (-float(keys[t, e]), e))[:k]
+            assert list(idx[t]) == ref
+            # the chosen set dominates the rest
+            chosen = set(ref)
+            rest = [e for e in range(7) if e not in chosen]
+            if rest:
+                assert min(keys[t, list(chosen)]) >= max(keys[t, rest])
+
+
+def test_topk_subset_bruteforce():
+    """The chosen set maximises the key sum over all k-subsets (distinct keys)."""
+    r = _rng(4)
+    keys = r.standard_normal((50, 6)).astype(np.float32)
+    idx, _, _ = O.topk_by_keys(keys, 3)
+    for t in range(50):
+        best = max(itertools.combinations(range(6), 3), key=lambda s: sum(float(keys[t, e]) for e in s))
+        assert set(idx[t]) == set(best)
+        # descending order of the chosen keys
+        assert all(keys[t, idx[t, j]] >= keys[t, idx[t, j + 1]] for j in range(2))
+
+
+def test_gaps():
+    keys = np.array([[5.0, 1.0, 3.0, 3.0, 0.5]], dtype=np.float32)
+    idx, gs, go = O.topk_by_keys(keys, 3)
+    assert list(idx[0]) == [0, 2, 3]
+    assert gs[0] == pytest.approx(2.0)        # 3 - 1
+    assert go[0] == 0.0                       # 3 - 3 is an order near-tie
+
+
+def test_softmax_then_topk_equals_topk_then_softmax():
+    """Identity: renormalised softmax-then-top-k (page P1's order) equals softmax over
+    the top-k logits (page P3's code), computed here with torch.softmax."""
+    r = _rng(5)
+    z = (3 * r.standard_normal((100, 16))).astype(np.float32)
+    rc = O.RouteConfig(E=16, k=4)
+    route = O.route_from_logits(z, rc)
+    probs = torch.softmax(torch.from_numpy(z.astype(np.float64)), dim=-1)
+    top = torch.topk(probs, 4, dim=-1)
+    ren = (top.values / top.values.sum(-1, keepdim=True)).numpy()
+    assert np.array_equal(top.indices.numpy(), route.idx)
+    np.testing.assert_allclose(route.w, ren, rtol=1e-6, atol=1e-7)
+
+
+def test_k_equals_E_gives_full_softmax():
+    r = _rng(6)
+    z = r.standard_normal((20, 8)).astype(np.float32)
+    for renorm in (0, 1):
+        rc = O.RouteConfig(E=8, k=8, renormalize=renorm)
+        route = O.route_from_logits(z, rc)
+        full = torch.softmax(torch.from_numpy(z.astype(np.float64)), -1).numpy()
+        got = np.zeros_like(full)
+        np.put_along_axis(got, route.idx.astype(np.int64), route.w.astype(np.float64), axis=1)
+        np.testing.assert_allclose(got, full, rtol=1e-6, atol=1e-8)
+        np.testing.assert_allclose(route.w.sum(1), 1.0, rtol=1e-6)
+
+
+def test_no_renormalisation_takes_topk_of_full_softmax():
+    """Page P1's router code: weights are the top-k entries of softmax over all E."""
+    r = _rng(7)
+    z = r.standard_normal((30, 16)).astype(np.float32)
+    rc = O.RouteConfig(E=16, k=2, renormalize=0, tau=0.5)
+    route = O.route_from_logits(z, rc)
+    full = torch.softmax(torch.from_numpy(z.astype(np.float64)) / 0.5, -1)
+    top = torch.topk(full, 2, -1)
+    assert np.array_equal(top.indices.numpy(), route.idx)
+    np.testing.assert_allclose(route.w, top.values.numpy(), rtol=1e-6)
+
+
+def test_gumbel_noise_closed_form_points():
+    """g(u) = -log(-log u): u = exp(-exp(-c)) gives c; u = 1/e gives 0."""
+    cs = np.array([-2.0, -0.5, 0.0, 0.7, 3.0], dtype=np.float64)
+    u = np.exp(-np.exp(-cs)).astype(np.float32)
+    g = O.gumbel_noise(u).astype(np.float64)
+    # u was rounded to float32: error propagates as |dg/du| * ulp(u)
+    du = np.abs(u.astype(np.float64) - np.exp(-np.exp(-cs)))
+    slope = 1.0 / (np.exp(-np.exp(-cs)) * np.exp(-cs))
+    assert np.all(np.abs(g - cs) <= slope * du + 1e-6)
+    assert abs(float(O.gumbel_noise(np.array([np.exp(-1)], np.float32))[0])) < 1e-7
+
+
+def test_gumbel_statistics_match_gumbel01():
+    """Mean of Gumbel(0,1) is the Euler-Mascheroni constant, variance pi^2/6; a
+    sign slip (Gumbel-min) flips the mean."""
+    from mixture_experts_sparse_amd import workloads as W
+    sh = W.WORKLOADS["gumbel_bf16"].replace(T=20000, E=16)
+    g = O.gumbel_noise(W.gumbel_uniforms(sh)).astype(np.float64).ravel()
+    assert abs(g.mean() - 0.5772156649) < 0.01
+    assert abs(g.var() - math.pi ** 2 / 6) < 0.03
+
+
+def test_gumbel_max_trick_samples_softmax():
+    """argmax(z + g) is distributed as softmax(z) (the Gumbel-max property)."""
+    r = _rng(8)
+    z = np.array([0.3, -0.2, 1.1, 0.0], dtype=np.float32)
+    n = 40000
+    m = r.integers(0, 1 << 23, size=(n, 4))
+    u = ((m + 0.5) * 2.0 ** -23).astype(np.float32)
+    rc = O.RouteConfig(E=4, k=1, tau=1.0)
+    route = O.route_from_logits(np.tile(z, (n, 1)), rc, u=u)
+    freq = np.bincount(route.idx[:, 0], minlength=4) / n
+    p = torch.softmax(torch.from_numpy(z.astype(np.float64)), -1).numpy()
+    assert np.all(np.abs(freq - p) < 0.01)
+
+
+def test_gumbel_zero_noise_reduces_to_tempered_softmax():
+    r = _rng(9)
+    z = r.standard_normal((64, 16)).astype(np.float32)
+    u = np.full((64, 16), np.float32(np.exp(-1.0)), dtype=np.float32)
+    rc = O.RouteConfig(E=16, k=2, tau=0.5, renormalize=0)
+    a = O.route_from_logits(z, rc, u=u)
+    b = O.route_from_logits(z, rc)
+    clear = b.gap_sel > 1e-5
+    assert np.array_equal(a.idx[clear], b.idx[clear])
+    np.testing.assert_allclose(a.w, b.w, rtol=1e-5)
+
+
+def test_sigmoid_selection_and_bias_invariance():
+    r = _rng(10)
+    z = r.standard_normal((100, 32)).astype(np.float32)
+    rc = O.RouteConfig(E=32, k=4, score=O.SCORE_SIGMOID, bias_mode=O.BIAS_SELECT_ONLY)
+    # constant bias: top-k of sigmoid(z) + c is the top-k of z (monotone)
+    a = O.route_from_logits(z, rc, bias=np.full(32, 0.25, np.float32))
+    idx_z, gs, _ = O.topk_by_keys(z, 4)
+    clear = gs > 1e-3
+    assert np.array_equal(a.idx[clear], idx_z[clear])
+    # weights are the unbiased sigmoid normalised over the chosen experts
+    s = 1.0 / (1.0 + np.exp(-z.astype(np.float64)))
+    ch = np.take_along_axis(s, a.idx.astype(np.int64), 1)
+    np.testing.assert_allclose(a.w, ch / ch.sum(1, keepdims=True), rtol=1e-6)
+    # a bias that changes nothing in the selection changes nothing in the weights
+    b = O.route_from_logits(z, rc, bias=np.zeros(32, np.float32))
+    same = np.all(a.idx == b.idx, axis=1)
+    np.testing.assert_array_equal(a.w[same], b.w[same])
+    assert float(O.sigmoid_scores(np.zeros(1, np.float32))[0]) == 0.5
+
+
+def test_selection_only_bias_steers_but_does_not_weigh():
+    z = np.array([[0.0, 0.1, 0.2, 0.3]], dtype=np.float32)
+    rc = O.RouteConfig(E=4, k=2, score=O.SCORE_SIGMOID, bias_mode=O.BIAS_SELECT_ONLY)
+    route = O.route_from_logits(z, rc, bias=np.array([5.0, 4.0, 0.0, 0.0], np.float32))
+    assert list(route.idx[0]) == [0, 1]
+    s0, s1 = 0.5, 1 / (1 + math.exp(-0.1))
+    np.testing.assert_allclose(route.w[0], [s0 / (s0 + s1), s1 / (s0 + s1)], rtol=1e-6)
+
+
+def test_logit_bias_enters_softmax():
+    z = np.zeros((1, 3), dtype=np.float32)
+    b = np.array([0.0, math.log(3.0), -10.0], np.float32)
+    rc = O.RouteConfig(E=3, k=2, bias_mode=O.BIAS_LOGIT)
+    route = O.route_from_logits(z, rc, bias=b)
+    assert list(route.idx[0]) == [1, 0]
+    np.testing.assert_allclose(route.w[0], [0.75, 0.25], rtol=1e-6)
+
+
+# ---------------------------------------------------------------- S3 capacity
+def test_capacity_worked_examples_from_pages():
+    with open(os.path.join(GOLDEN, "capacity_examples.json")) as f:
+        ex = json.load(f)["examples"]
+    for e in ex:
+        raw = e["tokens"] * e["k"] / e["experts"] * e["capacity_factor"]
+        assert raw == pytest.approx(e["raw"])
+        assert O.capacity(e["tokens"], e["k"], e["experts"], e["capacity_factor"]) == e["capacity"]
+
+
+def test_capacity_of_the_skewed_workload():
+    assert O.capacity(16384, 2, 128, 1.25) == 320
+    assert O.capacity(32, 2, 128, 1.25) == 1
+    assert O.capacity(64, 2, 8, 0.0) is None
+
+
+def _brute_permute(idx, E, C):
+    """Independent formulation: per-expert lists of pairs in (t, j) order, truncated."""
+    T, k = idx.shape
+    lists = [[] for _ in range(E)]
+    for t in range(T):
+        for j in range(k):
+            lists[idx[t, j]].append((t, j))
+    rows, dest = [], {}
+    for e in range(E):
+        keep = lists[e] if C is None else lists[e][:C]
+        for p in keep:
+            dest[p] = len(rows)
+            rows.append(p[0])
+    return lists, rows, dest
+
+
+@pytest.mark.parametrize("C", [None, 1, 3, 17])
+def test_permute_invariants_and_bruteforce(C):
+    r = _rng(11)
+    T, k, E = 97, 3, 9
+    idx = np.stack([r.choice(E, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    P = O.permute(idx, E, C)
+    lists, rows, dest = _brute_permute(idx, E, C)
+    assert P.counts.sum() == T * k
+    assert P.kept.sum() + P.n_dropped == T * k
+    assert list(P.counts) == [len(l) for l in lists]
+    if C is not None:
+        assert P.kept.max() <= C
+    assert P.offsets[0] == 0 and np.all(np.diff(P.offsets) >= 0) and P.offsets[-1] == P.kept.sum()
+    n = int(P.offsets[-1])
+    assert list(P.src_token[:n]) == rows and np.all(P.src_token[n:] == -1)
+    for t in range(T):
+        for j in range(k):
+            assert P.dest_row[t, j] == dest.get((t, j), -1)
+    # bijection from kept pairs onto rows 0..n-1
+    kept_rows = P.dest_row[P.dest_row >= 0]
+    assert sorted(kept_rows.tolist()) == list(range(n))
+    # inside each expert segment, tokens ascend
+    for e in range(E):
+        seg = P.src_token[P.offsets[e]:P.offsets[e + 1]]
+        assert np.all(np.diff(seg) > 0)
+
+
+def test_forced_overflow_closed_form():
+    """Every token sent to one expert with k = 1: exactly T - C dropped."""
+    T, E = 200, 16
+    for cf in (0.5, 1.0, 1.25, 3.0):
+        C = O.capacity(T, 1, E, cf)
+        idx = np.full((T, 1), 5, dtype=np.int32)
+        P = O.permute(idx, E, C)
+        assert P.n_dropped == T - min(T, C)
+        assert P.kept[5] == min(T, C)
+        # the first C tokens are the kept ones
+        assert np.all(P.dest_row[:C, 0] == np.arange(C)) and np.all(P.dest_row[C:, 0] == -1)
+
+
+def test_permutation_independent_of_slot_order():
+    """Rows depend on which experts a token chose, not on the order of its k slots."""
+    r = _rng(12)
+    idx = np.stack([r.choice(6, 2, replace=False) for _ in range(40)]).astype(np.int32)
+    a = O.permute(idx, 6, None)
+    b = O.permute(idx[:, ::-1].copy(), 6, None)
+    assert np.array_equal(a.src_token, b.src_token)
+    assert np.array_equal(a.dest_row, b.dest_row[:, ::-1])
+
+
+# ---------------------------------------------------------------- fp8
+def test_fp8_decode_all_codes():
+    codes = np.arange(256, dtype=np.uint8)
+    dec = O.fp8_e4m3fn_decode(codes)
+    lib = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(lib)
+    assert np.array_equal(np.isnan(dec), nan) and nan.sum() == 2
+    assert np.array_equal(dec[~nan], lib[~nan])
+    assert dec[0x7E] == 448.0 and dec[0x38] == 1.0 and dec[0x01] == 2.0 ** -9 and dec[0x08] == 2.0 ** -6
+    assert dec[0x80] == 0.0 and dec[0xFE] == -448.0
+
+
+# ---------------------------------------------------------------- S5/S6 experts
+def _dense_ffn_torch(x, wg, wu, wd):
+    """SwiGLU from torch's library routines (linear, silu) in float64."""
+    X = torch.from_numpy(np.asarray(x, np.float64))
+    g = torch.nn.functional.linear(X, torch.from_numpy(wg))
+    u = torch.nn.functional.linear(X, torch.from_numpy(wu))
+    return torch.nn.functional.linear(torch.nn.functional.silu(g) * u, torch.from_numpy(wd)).numpy()
+
+
+def _rand_experts(r, E, d, F):
+    return O.ExpertWeights((0.2 * r.standard_normal((E, F, d))),
+                           (0.2 * r.standard_normal((E, F, d))),
+                           (0.2 * r.standard_normal((E, d, F))))
+
+
+def test_single_expert_top1_is_dense_ffn():
+    r = _rng(13)
+    T, d, F = 33, 12, 20
+    x = r.standard_normal((T, d)).astype(np.float32)
+    ew = _rand_experts(r, 1, d, F)
+    spec = O.LayerSpec(T, d, 1, 1, F)
+    res = O.forward(spec, x, r.standard_normal((d, 1)).astype(np.float32), ew)
+    ref = _dense_ffn_torch(x, ew.w_gate[0], ew.w_up[0], ew.w_down[0])
+    np.testing.assert_allclose(res.out, ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("renorm", [1, 0])
+def test_identical_experts_reproduce_dense_ffn(renorm):
+    r = _rng(14)
+    T, d, F, E, k = 40, 10, 14, 6, 3
+    x = r.standard_normal((T, d)).astype(np.float32)
+    one = _rand_experts(r, 1, d, F)
+    ew = O.ExpertWeights(np.repeat(one.w_gate, E, 0), np.repeat(one.w_up, E, 0),
+                         np.repeat(one.w_down, E, 0))
+    spec = O.LayerSpec(T, d, E, k, F, renormalize=renorm)
+    res = O.forward(spec, x, r.standard_normal((d, E)).astype(np.float32), ew)
+    ref = _dense_ffn_torch(x, one.w_gate[0], one.w_up[0], one.w_down[0])
+    scale = res.routing.w.astype(np.float64).sum(1, keepdims=True)
+    if renorm:
+        np.testing.assert_allclose(scale, 1.0, rtol=1e-6)
+    np.testing.assert_allclose(res.out, scale * ref, rtol=1e-10, atol=1e-12)
+
+
+def test_grouped_experts_match_per_expert_dense():
+    """Each expert's rows of y_perm equal that expert's dense FFN (with d != F,
+    so a transposed operand cannot pass)."""
+    r = _rng(15)
+    T, d, F, E, k = 50, 8, 13, 5, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    ew = _rand_experts(r, E, d, F)
+    spec = O.LayerSpec(T, d, E, k, F)
+    res = O.forward(spec, x, r.standard_normal((d, E)).astype(np.float32), ew)
+    for e in range(E):
+        a, b = res.perm.offsets[e], res.perm.offsets[e + 1]
+        toks = res.perm.src_token[a:b]
+        ref = _dense_ffn_torch(x[toks], ew.w_gate[e], ew.w_up[e], ew.w_down[e])
+        np.testing.assert_allclose(res.y_perm[a:b], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_swiglu_bruteforce_tiny():
+    """Scalar loops with math.exp on a 2x3 -> 4 -> 3 case."""
+    r = _rng(16)
+    x = r.standard_normal((2, 3))
+    wg, wu, wd = r.standard_normal((4, 3)), r.standard_normal((4, 3)), r.standard_normal((3, 4))
+    y = O.swiglu_ffn(x, wg, wu, wd)
+    for t in range(2):
+        h = []
+        for f in range(4):
+            g = sum(x[t, i] * wg[f, i] for i in range(3))
+            u = sum(x[t, i] * wu[f, i] for i in range(3))
+            h.append(g / (1 + math.exp(-g)) * u)
+        for o in range(3):
+            assert y[t, o] == pytest.approx(sum(h[f] * wd[o, f] for f in range(4)), rel=1e-12)
+
+
+def test_fp8_expert_dequant_uses_row_scales():
+    codes = np.array([[0x38, 0xB8], [0x40, 0x30]], dtype=np.uint8)  # 1, -1 ; 2, 0.5
+    w = O.dequant(codes, np.array([0.5, 3.0]))
+    np.testing.assert_array_equal(w, [[0.5, -0.5], [6.0, 1.5]])
+
+
+# ---------------------------------------------------------------- S7 combine
+def test_identity_expert_combine_inverts_permute():
+    """With y := x_perm, renormalised weights and no drops, combine(permute(x)) = x."""
+    r = _rng(17)
+    T, d, E, k = 70, 9, 7, 3
+    x = r.standard_normal((T, d))
+    z = r.standard_normal((T, E)).astype(np.float32)
+    route = O.route_from_logits(z, O.RouteConfig(E, k))
+    P = O.permute(route.idx, E, None)
+    xp = x[P.src_token[:P.offsets[-1]]]
+    out = O.combine(xp, P.dest_row, route.w)
+    np.testing.assert_allclose(out, x * route.w.astype(np.float64).sum(1, keepdims=True), rtol=1e-12)
+    np.testing.assert_allclose(out, x, rtol=1e-6, atol=1e-6)
+
+
+def test_dropped_tokens_get_zero_plus_shared():
+    T, d, E = 12, 4, 3
+    idx = np.zeros((T, 1), dtype=np.int32)
+    w = np.ones((T, 1), dtype=np.float32)
+    P = O.permute(idx, E, 5)
+    y = np.arange(5 * d, dtype=np.float64).reshape(5, d) + 1
+    out = O.combine(y, P.dest_row, w)
+    assert np.all(out[5:] == 0) and np.array_equal(out[:5], y)
+    sh = np.full((T, d), 7.0)
+    out2 = O.combine(y, P.dest_row, w, sh)
+    assert np.all(out2[5:] == 7.0)
+
+
+def test_token_outputs_agree_with_forward():
+    r = _rng(18)
+    T, d, F, E, k = 30, 8, 6, 4, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    ew = _rand_experts(r, E, d, F)
+    sh = _rand_experts(r, 1, d, F)
+    spec = O.LayerSpec(T, d, E, k, F, n_shared=1, capacity_factor=1.0)
+    res = O.forward(spec, x, r.standard_normal((d, E)).astype(np.float32), ew, sh)
+    toks = [0, 3, 29, 17]
+    got = O.token_outputs(toks, x, res.perm.dest_row, res.routing.idx, res.routing.w, ew, sh)
+    np.testing.assert_allclose(got, res.out[toks], rtol=1e-12, atol=1e-12)
