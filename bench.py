@@ -1,0 +1,227 @@
+"""Benchmark of the sparse MoE layer on one MI355X.
+
+One step = one moe_forward call (route -> top-k -> capacity-limited permute ->
+grouped SwiGLU experts -> weighted combine) over one batch of seeded synthetic
+input already resident in HBM.  Prints one JSON line:
+
+  value       tokens per second of the whole layer (T / step time)
+  roofline    the dominant kernel's achieved rate from HIP events recorded
+              around each launch on its stream during the timed steps, against
+              the MI355X peak for its bound
+  kernels     the same for every kernel of the step (average duration,
+              algorithmic FLOP or bytes per launch, rate, fraction of peak)
+  cpu_baseline the CPU oracle on a bounded sample of the same workload
+
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload mixtral_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s; grouped-GEMM % MFMA peak; permute/combine % HBM BW"
+PEAK_HBM_GBS = 8000.0
+PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
+DEFAULT_WORKLOAD = "mixtral_bf16"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a plain 512 MiB device copy first (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def algorithmic_work(sh, kept_rows: int, touched: int):
+    """Per-launch algorithmic FLOP and HBM bytes of each kernel (each tensor once)."""
+    from mixture_experts_sparse_amd import workloads as W
+    a = W.nbytes_of(sh.act_dtype)
+    wb = W.nbytes_of(sh.w_dtype)
+    hb = 4 if sh.w_dtype == W.DT_F32 else 2
+    T, d, E, k, F, N = sh.T, sh.d, sh.E, sh.k, sh.F, kept_rows
+    scale_b = 4 * (2 * F + d) if sh.w_dtype == W.DT_FP8 else 0
+    work = {
+        # router: x once, W_r once, logits/indices/weights out
+        "route_topk": {"flop": 2.0 * T * d * E, "bytes": T * d * a + d * E * 4 + T * k * 8},
+        "permute_hist": {"bytes": T * k * 4},
+        "permute_scan": {"bytes": 0},
+        "permute_rank": {"bytes": T * k * 8 + N * 4},
+        # read each token row once, write each kept copy once
+        "permute_scatter": {"bytes": T * d * a + N * d * a + T * k * 4},
+        "gemm_tiles": {"bytes": 0},
+        # gate/up: x_perm read, both weight matrices of every touched expert, h written
+        "gemm_gate_up": {"flop": 4.0 * N * d * F,
+                         "bytes": N * d * a + touched * (2 * F * d * wb) + touched * scale_b + N * F * hb},
+        "gemm_down": {"flop": 2.0 * N * F * d,
+                      "bytes": N * F * hb + touched * (d * F * wb) + N * d * 4},
+        # kept rows of y (f32) read once, output written once (+ shared rows)
+        "combine": {"bytes": N * d * 4 + T * d * (4 if sh.out_dtype == W.DT_F32 else 2)
+                    + T * k * 8 + (T * d * 4 if sh.n_shared else 0)},
+    }
+    if sh.n_shared:
+        work["shared_gate_up"] = {"flop": 4.0 * T * d * F, "bytes": T * d * a + 2 * F * d * wb + T * F * hb}
+        work["shared_down"] = {"flop": 2.0 * T * F * d, "bytes": T * F * hb + d * F * wb + T * d * 4}
+    return work
+
+
+def kernel_key(name: str) -> str:
+    """Library kernel name -> work key (drops the dtype tags)."""
+    n = name.replace("_f32", "").replace("_bf16", "").replace("_fp8", "")
+    return n
+
+
+def cpu_baseline(inp, sample: int):
+    """Time the CPU oracle (as it stands) on the first `sample` tokens."""
+    import numpy as np
+    import threadpoolctl
+
+    from oracle import from_inputs as FI
+    from oracle import moe_oracle as O
+
+    sh = inp.shape
+    cpu = inp.to("cpu")
+    x = FI.to_np(cpu.x)[:sample]
+    u = FI.to_np(cpu.gumbel_u)
+    u = None if u is None else u[:sample]
+    ew = FI.expert_weights(cpu)
+    shw = FI.shared_weights(cpu)
+    wr, b = FI.to_np(cpu.w_router), FI.to_np(cpu.bias)
+    spec = FI.layer_spec(sh.replace(T=sample))
+    t0 = time.perf_counter()
+    O.forward(spec, x, wr, ew, shw, b, u)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {sample} of {sh.T} tokens of {sh.name} (capacity recomputed for the "
+                      f"sample), full layer in float64 numpy; {dt:.2f} s wall"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer's multi-GPU "
+              "sharding is a design note, not a measured path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from mixture_experts_sparse_amd import load
+    from mixture_experts_sparse_amd import workloads as W
+
+    L = load()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda:0")
+    sh = W.WORKLOADS[args.workload]
+    print(f"[bench] workload {sh.name}: T={sh.T} d={sh.d} E={sh.E} k={sh.k} F={sh.F}", file=sys.stderr, flush=True)
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    inp = W.make_inputs(sh, device=dev)
+    cfg = L.make_config(sh)
+    weights = L.expert_weights(inp)
+    ws = L.alloc_workspace(cfg, dev)
+    out = torch.empty((sh.T, sh.d), dtype=torch.float32, device=dev)
+    stats = torch.empty(2 * sh.E + 1, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    print("[bench] inputs ready", file=sys.stderr, flush=True)
+
+    def step():
+        L.moe_forward(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, weights, out, stats, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    L.moe_profile_read()  # discard anything recorded before
+    L.moe_profile_enable(True)
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    stop.record()
+    torch.cuda.synchronize()
+    L.moe_profile_enable(False)
+    prof = L.moe_profile_read()
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / args.steps
+    st = stats.cpu().numpy()
+    kept = int(st[sh.E:2 * sh.E].sum())
+    touched = int((st[sh.E:2 * sh.E] > 0).sum())
+    work = algorithmic_work(sh, kept, touched)
+    dt_name = {W.DT_BF16: "bf16", W.DT_FP8: "fp8", W.DT_F32: "f32"}[sh.w_dtype]
+    mfma_peak = PEAK_TFLOPS["bf16" if sh.w_dtype == W.DT_FP8 else dt_name]
+
+    kernels = {}
+    for name, (launches, total_ms) in prof.items():
+        per_step = launches / args.steps
+        avg_us = 1000.0 * total_ms / launches
+        wk = work.get(kernel_key(name), {})
+        flop = wk.get("flop", 0.0)
+        byts = wk.get("bytes", 0)
+        ent = {"launches_per_step": per_step, "avg_us": round(avg_us, 2)}
+        if flop:
+            tf = flop / (avg_us * 1e-6) / 1e12
+            ent.update({"tflops": round(tf, 1), "mfma_frac": round(tf / mfma_peak, 4)})
+        if byts:
+            gbs = byts / (avg_us * 1e-6) / 1e9
+            ent.update({"gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+        kernels[name] = ent
+
+    # dominant kernel: the largest share of the step time
+    dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
+    dk = kernels[dom]
+    if "tflops" in dk and ("gate_up" in dom or "down" in dom):
+        roof = {"kernel": dom, "bound": "mfma", "achieved": dk["tflops"], "peak": mfma_peak,
+                "unit": "TFLOP/s", "frac": dk["mfma_frac"], "traffic": None}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": dk.get("gbs"), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": dk.get("hbm_frac"), "traffic": None}
+
+    res = {
+        "metric": METRIC,
+        "value": round(sh.T / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic",
+        "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "E": sh.E, "top_k": sh.k, "F": sh.F,
+                   "n_shared": sh.n_shared, "weights": dt_name, "router": "f32",
+                   "capacity_factor": sh.capacity_factor or None, "kept_rows": kept,
+                   "touched_experts": touched, "dropped": int(st[2 * sh.E])},
+        "roofline": roof,
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        sample = args.cpu_sample or min(sh.T, 256)
+        print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, sample)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

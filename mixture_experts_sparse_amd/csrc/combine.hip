@@ -1,0 +1,74 @@
+// Weighted combine of the expert outputs back into token order.
+//
+// Page "MoE sparse activation: principles and engineering practice"
+// (kapook.pages.dev), s3.1: the layer output is the sum over the chosen
+// experts of gate weight times expert output.  Page "From sparse MoE to
+// conditional memory" (m.nxbn.cn), aggregation layer: weighted combine (the
+// residual add is the caller's).  Page "V4 full-stack architecture"
+// (kwkr.cn), s2.2: the shared expert every token visits, added with weight 1.
+//
+//   out[t] = sum_{j: dest_row[t,j] >= 0} w[t,j] * y_perm[dest_row[t,j]]  (+ y_shared[t])
+//
+// Bandwidth-bound: one wave per token, 16-byte vector loads of the k source
+// rows (gathered by dest_row), f32 FMAs in j order, one store of the row.
+#include "common.h"
+
+namespace moe {
+namespace {
+
+template <bool BF16OUT>
+__global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm,
+                                                      const float4* __restrict__ y_shared,
+                                                      const int32_t* __restrict__ dest_row,
+                                                      const float* __restrict__ topk_w,
+                                                      void* __restrict__ out, int T, int vec_per_row,
+                                                      int k, int64_t rows) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int32_t* dr = dest_row + (size_t)t * k;
+  const float* wt = topk_w + (size_t)t * k;
+  for (int v = lane; v < vec_per_row; v += 64) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const int row = dr[j];
+      if (row < 0 || row >= rows) continue;  // dropped (or out of range: ignored)
+      const float w = wt[j];
+      const float4 y = y_perm[(size_t)row * vec_per_row + v];
+      acc.x = fmaf(w, y.x, acc.x);
+      acc.y = fmaf(w, y.y, acc.y);
+      acc.z = fmaf(w, y.z, acc.z);
+      acc.w = fmaf(w, y.w, acc.w);
+    }
+    if (y_shared) {
+      const float4 s = y_shared[(size_t)t * vec_per_row + v];
+      acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
+    }
+    if (BF16OUT) {
+      uint2 o;
+      o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+      o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+      ((uint2*)out)[(size_t)t * vec_per_row + v] = o;
+    } else {
+      ((float4*)out)[(size_t)t * vec_per_row + v] = acc;
+    }
+  }
+}
+
+}  // namespace
+
+moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows) {
+  if (a.T == 0) return MOE_OK;
+  const int vec = a.d / 4;
+  const dim3 grid((unsigned)ceil_div(a.T, 4));
+  int tok = begin_launch("combine", s);
+  if (a.out_dtype == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, (const float4*)a.y_perm,
+                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, (const float4*)a.y_perm,
+                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows);
+  return end_launch(tok, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,127 @@
+// Internal helpers shared by the HIP kernels of the MoE layer (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- vectors
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+
+constexpr int kWave = 64;
+
+// bf16 <-> f32 (bit-level; bf16 is the top half of an f32)
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
+  return __uint_as_float(b << 16);
+}
+__host__ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// MFMA 16x16x32 bf16 -> f32.  Lane l supplies A[m = l%16][8 k-values of group l/16]
+// and B[the same 8 k-values][n = l%16]; it receives D[m = 4*(l/16) + r][n = l%16]
+// in element r.  A and B use one k-mapping, so the sum over k is exact whatever
+// order the hardware assigns within a group.
+__device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b,
+                                                const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// Two OCP e4m3fn codes (bytes 0,1 of `packed`, or bytes 2,3 when HIGH) -> two bf16;
+// exact (fp8 values are a subset of bf16), hardware conversion with unit scale.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t packed) {
+  bf16x2_t v = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(packed, 1.0f, HIGH);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// 16 e4m3fn codes (one uint4) -> 16 bf16 (two uint4), element order preserved.
+__device__ __forceinline__ void fp8x16_to_bf16x16(const uint4& q, uint4& lo, uint4& hi) {
+  lo.x = fp8x2_to_bf16x2<false>(q.x);
+  lo.y = fp8x2_to_bf16x2<true>(q.x);
+  lo.z = fp8x2_to_bf16x2<false>(q.y);
+  lo.w = fp8x2_to_bf16x2<true>(q.y);
+  hi.x = fp8x2_to_bf16x2<false>(q.z);
+  hi.y = fp8x2_to_bf16x2<true>(q.z);
+  hi.z = fp8x2_to_bf16x2<false>(q.w);
+  hi.w = fp8x2_to_bf16x2<true>(q.w);
+}
+
+__device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
+
+// ---------------------------------------------------------------- host side
+// Record a launch for the profiling hook; returns an index for end_launch().
+int begin_launch(const char* name, hipStream_t s);
+// Checks hipGetLastError() after a launch; closes the profiling bracket.
+moe_status end_launch(int token, hipStream_t s);
+// Thread-local error message setter.
+moe_status fail(moe_status st, const char* fmt, ...);
+// Number of compute units on the current device (cached per device).
+int device_cu_count();
+
+// Integer helpers
+__host__ __device__ constexpr inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+__host__ __device__ constexpr inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- kernel launchers
+// Implemented in the .hip files; every launcher returns MOE_OK or MOE_ERR_HIP.
+struct RouteLaunch {
+  const void* x; const float* w_router; const float* bias; const float* gumbel_u;
+  float* logits; int32_t* topk_idx; float* topk_w;
+  int T, d, E, k, score, renormalize, bias_mode, act_dtype;
+  float tau;
+};
+moe_status launch_route(const RouteLaunch& a, hipStream_t s);
+
+// Permutation geometry: pairs are processed in chunks of kPermChunk.
+constexpr int kPermChunk = 1024;
+struct PermuteLaunch {
+  const void* x; const int32_t* topk_idx;
+  int32_t* counts; int32_t* offsets; int32_t* dest_row; int32_t* src_token; int32_t* n_dropped;
+  void* x_perm;
+  int32_t* stats;        // [2E+1] or null
+  int32_t* hist;         // workspace [nblocks * E]
+  int T, d, E, k, act_bytes;
+  int64_t capacity;      // < 0: no limit
+  int64_t rows;          // permuted rows provided by the caller
+};
+moe_status launch_permute(const PermuteLaunch& a, hipStream_t s);
+
+struct CombineLaunch {
+  const float* y_perm; const float* y_shared; const int32_t* dest_row; const float* topk_w;
+  void* out; int T, d, k, out_dtype;
+};
+// rows: size of y_perm; destinations outside [0, rows) are ignored
+moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows);
+
+// Grouped GEMM over experts.  Rows of group g are [offsets[g], offsets[g+1]) of A
+// (or [0, single_rows) when offsets == null).  B is [groups][n_b][K] ([out, in]).
+struct GemmLaunch {
+  const void* A;            // [rows, K] bf16 or f32
+  const void* B0;           // gate (gated) or down weights
+  const void* B1;           // up weights (gated) or null
+  const float* S0;          // fp8 row scales for B0 [groups][n_b] or null
+  const float* S1;
+  void* out;                // gated: h [rows, F] (bf16 or f32); else y [rows, N] f32
+  const int32_t* offsets;   // [groups+1] or null
+  int32_t* tile_prefix;     // workspace [2 * (groups+1)]: sanitised offsets, tile prefix
+  int groups;
+  int single_rows;          // rows when offsets == null
+  int64_t max_rows;         // upper bound on rows (grid sizing)
+  int K;                    // reduction size
+  int N;                    // output columns (F for gated, d for down)
+  int w_dtype;              // MOE_F32 / MOE_BF16 / MOE_FP8_E4M3FN
+  bool gated;
+  bool shared;              // the shared expert (names its launches apart)
+};
+moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+
+}  // namespace moe

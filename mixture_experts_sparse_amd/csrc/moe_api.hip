@@ -1,0 +1,453 @@
+// C-ABI entry points of the MoE layer: host-side validation, workspace
+// carving and launch sequencing.  See include/moe.h for the contract.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------- errors
+namespace {
+thread_local char g_err[512] = "";
+}
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+// ---------------------------------------------------------------- device info
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    cache[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- profiling hook
+namespace {
+struct ProfRec {
+  const char* name;
+  hipEvent_t start, stop;
+};
+thread_local bool g_prof = false;
+thread_local std::vector<ProfRec> g_recs;
+thread_local std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+}  // namespace
+
+int begin_launch(const char* name, hipStream_t s) {
+  if (!g_prof) return -1;
+  ProfRec r{name, take_event(), take_event()};
+  if (!r.start || !r.stop) return -1;
+  hipEventRecord(r.start, s);
+  g_recs.push_back(r);
+  return (int)g_recs.size() - 1;
+}
+
+moe_status end_launch(int tok, hipStream_t s) {
+  const hipError_t e = hipGetLastError();
+  if (tok >= 0 && tok < (int)g_recs.size()) hipEventRecord(g_recs[tok].stop, s);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+// ---------------------------------------------------------------- validation and layout
+namespace {
+
+int dtype_bytes(int dt) { return dt == MOE_F32 ? 4 : dt == MOE_BF16 ? 2 : 1; }
+
+moe_status check_config(const moe_config* c) {
+  if (!c) return fail(MOE_ERR_INVALID_ARGUMENT, "cfg is NULL");
+  if (c->T < 0) return fail(MOE_ERR_INVALID_ARGUMENT, "T = %d < 0", c->T);
+  if (c->E < 1 || c->E > 256) return fail(MOE_ERR_INVALID_ARGUMENT, "E = %d outside [1, 256]", c->E);
+  if (c->top_k < 1 || c->top_k > c->E)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "top_k = %d outside [1, E = %d]", c->top_k, c->E);
+  if (c->d <= 0 || c->F <= 0) return fail(MOE_ERR_INVALID_ARGUMENT, "d = %d, F = %d must be > 0", c->d, c->F);
+  if (c->n_shared != 0 && c->n_shared != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "n_shared = %d must be 0 or 1", c->n_shared);
+  if ((int64_t)c->T * c->top_k >= (int64_t)1 << 31)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "T * top_k must be < 2^31");
+  if (c->score != MOE_SCORE_SOFTMAX && c->score != MOE_SCORE_SIGMOID)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "score = %d", c->score);
+  if (c->renormalize != 0 && c->renormalize != 1)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "renormalize = %d must be 0 or 1", c->renormalize);
+  if (!(c->tau > 0.f) || !std::isfinite(c->tau))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "tau = %g must be finite and > 0", (double)c->tau);
+  if (c->bias_mode < MOE_BIAS_NONE || c->bias_mode > MOE_BIAS_SELECT_ONLY)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "bias_mode = %d", c->bias_mode);
+  if (c->score == MOE_SCORE_SIGMOID && (c->tau != 1.f || c->bias_mode == MOE_BIAS_LOGIT))
+    return fail(MOE_ERR_UNSUPPORTED, "sigmoid scoring takes tau = 1 and no logit bias");
+  if (!std::isfinite(c->capacity_factor))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "capacity_factor must be finite");
+  if (c->act_dtype != MOE_F32 && c->act_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "act_dtype = %d", c->act_dtype);
+  if (c->out_dtype != MOE_F32 && c->out_dtype != MOE_BF16)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "out_dtype = %d", c->out_dtype);
+  if (c->w_dtype == MOE_F32) {
+    if (c->act_dtype != MOE_F32) return fail(MOE_ERR_UNSUPPORTED, "fp32 weights need fp32 activations");
+    if (c->F % 32) return fail(MOE_ERR_UNSUPPORTED, "F = %d must be a multiple of 32 for fp32 weights", c->F);
+  } else if (c->w_dtype == MOE_BF16 || c->w_dtype == MOE_FP8_E4M3FN) {
+    if (c->act_dtype != MOE_BF16)
+      return fail(MOE_ERR_UNSUPPORTED, "bf16/fp8 weights need bf16 activations");
+    if (c->F % 64) return fail(MOE_ERR_UNSUPPORTED, "F = %d must be a multiple of 64", c->F);
+  } else {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "w_dtype = %d", c->w_dtype);
+  }
+  if (c->d % 128) return fail(MOE_ERR_UNSUPPORTED, "d = %d must be a multiple of 128", c->d);
+  return MOE_OK;
+}
+
+// C = max(1, floor(T*k/E*cf)) in double from the float32 factor; -1 = no limit.
+int64_t capacity_of(const moe_config* c) {
+  if (!(c->capacity_factor > 0.f)) return -1;
+  const double v = std::floor((double)c->T * (double)c->top_k / (double)c->E * (double)c->capacity_factor);
+  return v < 1.0 ? 1 : (int64_t)v;
+}
+
+int64_t perm_rows(const moe_config* c) {
+  const int64_t pairs = (int64_t)c->T * c->top_k;
+  const int64_t cap = capacity_of(c);
+  if (cap < 0) return pairs;
+  return std::min<int64_t>(pairs, cap * c->E);
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+struct Layout {
+  // permute / ffn scratch
+  size_t hist, tiles, tiles_sh, h, h_sh;
+  // forward intermediates
+  size_t logits, idx, w, counts, offsets, dest, src, ndrop, x_perm, y_perm, y_sh;
+  size_t perm_end, ffn_end, total;
+};
+
+Layout layout_of(const moe_config* c) {
+  Layout L{};
+  const int64_t R = perm_rows(c);
+  const int64_t P = (int64_t)c->T * c->top_k;
+  const int64_t nblk = std::max<int64_t>(1, ceil_div(P, kPermChunk));
+  const size_t hb = c->w_dtype == MOE_F32 ? 4 : 2;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  // scratch shared by moe_permute and moe_expert_ffn (they never run concurrently
+  // on one workspace within moe_forward; standalone callers pass one each)
+  L.hist = take(sizeof(int32_t) * nblk * c->E);
+  L.perm_end = o;
+  L.tiles = take(sizeof(int32_t) * 2 * (c->E + 1));
+  L.tiles_sh = take(sizeof(int32_t) * 4);
+  L.h = take(hb * R * c->F);
+  L.h_sh = take(c->n_shared ? hb * (size_t)c->T * c->F : 0);
+  L.ffn_end = o;
+  L.logits = take(sizeof(float) * (size_t)c->T * c->E);
+  L.idx = take(sizeof(int32_t) * P);
+  L.w = take(sizeof(float) * P);
+  L.counts = take(sizeof(int32_t) * c->E);
+  L.offsets = take(sizeof(int32_t) * (c->E + 1));
+  L.dest = take(sizeof(int32_t) * P);
+  L.src = take(sizeof(int32_t) * std::max<int64_t>(R, 1));
+  L.ndrop = take(sizeof(int32_t));
+  L.x_perm = take((size_t)dtype_bytes(c->act_dtype) * R * c->d);
+  L.y_perm = take(sizeof(float) * R * c->d);
+  L.y_sh = take(c->n_shared ? sizeof(float) * (size_t)c->T * c->d : 0);
+  L.total = o;
+  return L;
+}
+
+moe_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return MOE_OK;
+  if (!ws) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace is NULL (%zu bytes needed)", need);
+  if ((uintptr_t)ws & 255u) return fail(MOE_ERR_INVALID_ARGUMENT, "workspace must be 256-byte aligned");
+  if (have < need) return fail(MOE_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", have, need);
+  return MOE_OK;
+}
+
+moe_status check_weights(const moe_config* c, const moe_expert_weights* w) {
+  if (!w) return fail(MOE_ERR_INVALID_ARGUMENT, "weights is NULL");
+  if (!w->w_gate || !w->w_up || !w->w_down) return fail(MOE_ERR_INVALID_ARGUMENT, "expert weight pointer is NULL");
+  if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "expert weights must be 16-byte aligned");
+  const bool fp8 = c->w_dtype == MOE_FP8_E4M3FN;
+  if (fp8 != (w->s_gate && w->s_up && w->s_down) || (!fp8 && (w->s_gate || w->s_up || w->s_down)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "row scales are required for fp8 weights and only for them");
+  if (c->n_shared) {
+    if (!w->sh_gate || !w->sh_up || !w->sh_down) return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights missing");
+    if (!aligned16(w->sh_gate) || !aligned16(w->sh_up) || !aligned16(w->sh_down))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights must be 16-byte aligned");
+    if (fp8 != (w->sh_s_gate && w->sh_s_up && w->sh_s_down))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert row scales are required for fp8 weights");
+  } else if (w->sh_gate || w->sh_up || w->sh_down) {
+    return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights given but n_shared == 0");
+  }
+  return MOE_OK;
+}
+
+moe_status check_route_args(const moe_config* c, const void* x, const float* w_router, const float* bias,
+                            const float* gumbel_u, const int32_t* topk_idx, const float* topk_w) {
+  if (c->T > 0) {
+    if (!x || !w_router || !topk_idx || !topk_w) return fail(MOE_ERR_INVALID_ARGUMENT, "route pointer is NULL");
+    if (!aligned16(x)) return fail(MOE_ERR_INVALID_ARGUMENT, "x must be 16-byte aligned");
+  }
+  if ((c->bias_mode != MOE_BIAS_NONE) != (bias != nullptr))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "bias must be given exactly when bias_mode != NONE");
+  if (gumbel_u && c->score != MOE_SCORE_SOFTMAX)
+    return fail(MOE_ERR_UNSUPPORTED, "Gumbel noise applies to softmax scoring only");
+  return MOE_OK;
+}
+
+// ---- step runners shared by the standalone entry points and moe_forward
+moe_status run_route(const moe_config* c, const void* x, const float* w_router, const float* bias,
+                     const float* gumbel_u, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  RouteLaunch r{x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, c->T, c->d, c->E, c->top_k,
+                c->score, c->renormalize, c->bias_mode, c->act_dtype, c->tau};
+  return launch_route(r, s);
+}
+
+moe_status run_permute(const moe_config* c, const void* x, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* dest_row, int32_t* src_token, int32_t* n_dropped,
+                       void* x_perm, int32_t* stats, char* ws, hipStream_t s) {
+  const Layout L = layout_of(c);
+  PermuteLaunch p{x, topk_idx, counts, offsets, dest_row, src_token, n_dropped, x_perm, stats,
+                  (int32_t*)(ws + L.hist), c->T, c->d, c->E, c->top_k, dtype_bytes(c->act_dtype),
+                  capacity_of(c), perm_rows(c)};
+  return launch_permute(p, s);
+}
+
+moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const int32_t* offsets,
+                   const moe_expert_weights* w, float* y_perm, float* y_shared, char* ws, hipStream_t s) {
+  if (c->T == 0) return MOE_OK;
+  const Layout L = layout_of(c);
+  const int64_t R = perm_rows(c);
+  GemmLaunch g{};
+  g.w_dtype = c->w_dtype;
+  // routed experts: gate/up pass then down pass
+  g.A = x_perm; g.B0 = w->w_gate; g.B1 = w->w_up; g.S0 = w->s_gate; g.S1 = w->s_up;
+  g.out = ws + L.h; g.offsets = offsets; g.tile_prefix = (int32_t*)(ws + L.tiles);
+  g.groups = c->E; g.single_rows = 0; g.max_rows = R; g.K = c->d; g.N = c->F; g.gated = true;
+  moe_status st = launch_grouped_gemm(g, s);
+  if (st != MOE_OK) return st;
+  g.A = ws + L.h; g.B0 = w->w_down; g.B1 = nullptr; g.S0 = w->s_down; g.S1 = nullptr;
+  g.out = y_perm; g.K = c->F; g.N = c->d; g.gated = false;
+  st = launch_grouped_gemm(g, s);
+  if (st != MOE_OK || !c->n_shared) return st;
+  // shared expert over all tokens
+  g.A = x; g.B0 = w->sh_gate; g.B1 = w->sh_up; g.S0 = w->sh_s_gate; g.S1 = w->sh_s_up;
+  g.out = ws + L.h_sh; g.offsets = nullptr; g.tile_prefix = (int32_t*)(ws + L.tiles_sh);
+  g.groups = 1; g.single_rows = c->T; g.max_rows = c->T; g.K = c->d; g.N = c->F; g.gated = true;
+  g.shared = true;
+  st = launch_grouped_gemm(g, s);
+  if (st != MOE_OK) return st;
+  g.A = ws + L.h_sh; g.B0 = w->sh_down; g.B1 = nullptr; g.S0 = w->sh_s_down; g.S1 = nullptr;
+  g.out = y_shared; g.K = c->F; g.N = c->d; g.gated = false;
+  return launch_grouped_gemm(g, s);
+}
+
+moe_status run_combine(const moe_config* c, const float* y_perm, const float* y_shared,
+                       const int32_t* dest_row, const float* topk_w, void* out, hipStream_t s) {
+  CombineLaunch cl{y_perm, c->n_shared ? y_shared : nullptr, dest_row, topk_w, out, c->T, c->d, c->top_k,
+                   c->out_dtype};
+  return launch_combine(cl, s, perm_rows(c));
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MOE_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* moe_last_error(void) { return g_err; }
+
+int32_t moe_version(void) { return 100; }
+
+moe_status moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!bytes) return fail(MOE_ERR_INVALID_ARGUMENT, "bytes is NULL");
+  *bytes = layout_of(cfg).total;
+  return MOE_OK;
+}
+
+moe_status moe_permuted_rows(const moe_config* cfg, int64_t* rows) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!rows) return fail(MOE_ERR_INVALID_ARGUMENT, "rows is NULL");
+  *rows = perm_rows(cfg);
+  return MOE_OK;
+}
+
+moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
+                     const float* gumbel_u, float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st == MOE_OK) st = check_route_args(cfg, x, w_router, bias, gumbel_u, topk_idx, topk_w);
+  if (st != MOE_OK) return st;
+  return run_route(cfg, x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, (hipStream_t)stream);
+}
+
+moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
+                       int32_t* offsets, int32_t* dest_row, int32_t* src_token, int32_t* n_dropped,
+                       void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!counts || !offsets || !n_dropped) return fail(MOE_ERR_INVALID_ARGUMENT, "permute output pointer is NULL");
+  if (cfg->T > 0) {
+    if (!x || !topk_idx || !dest_row || !src_token || !x_perm)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "permute pointer is NULL");
+    if (!aligned16(x) || !aligned16(x_perm)) return fail(MOE_ERR_INVALID_ARGUMENT, "x and x_perm must be 16-byte aligned");
+  }
+  st = check_ws(ws, ws_bytes, layout_of(cfg).perm_end);
+  if (st != MOE_OK) return st;
+  return run_permute(cfg, x, topk_idx, counts, offsets, dest_row, src_token, n_dropped, x_perm, nullptr,
+                     (char*)ws, (hipStream_t)stream);
+}
+
+moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_perm, const int32_t* offsets,
+                          const moe_expert_weights* weights, float* y_perm, float* y_shared, void* ws,
+                          size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st == MOE_OK) st = check_weights(cfg, weights);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0) {
+    if (!x_perm || !offsets || !y_perm) return fail(MOE_ERR_INVALID_ARGUMENT, "expert_ffn pointer is NULL");
+    if (!aligned16(x_perm) || !aligned16(y_perm)) return fail(MOE_ERR_INVALID_ARGUMENT, "x_perm and y_perm must be 16-byte aligned");
+    if (cfg->n_shared && (!x || !y_shared || !aligned16(x) || !aligned16(y_shared)))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "x and y_shared (16-byte aligned) are required with a shared expert");
+  }
+  st = check_ws(ws, ws_bytes, layout_of(cfg).ffn_end);
+  if (st != MOE_OK) return st;
+  return run_ffn(cfg, x, x_perm, offsets, weights, y_perm, y_shared, (char*)ws, (hipStream_t)stream);
+}
+
+moe_status moe_combine(const moe_config* cfg, const float* y_perm, const float* y_shared, const int32_t* dest_row,
+                       const float* topk_w, void* out, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0) {
+    if (!y_perm || !dest_row || !topk_w || !out) return fail(MOE_ERR_INVALID_ARGUMENT, "combine pointer is NULL");
+    if (!aligned16(y_perm) || !aligned16(out)) return fail(MOE_ERR_INVALID_ARGUMENT, "y_perm and out must be 16-byte aligned");
+    if (cfg->n_shared && (!y_shared || !aligned16(y_shared)))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "y_shared (16-byte aligned) is required with a shared expert");
+  }
+  return run_combine(cfg, y_perm, y_shared, dest_row, topk_w, out, (hipStream_t)stream);
+}
+
+moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
+                       const float* gumbel_u, const moe_expert_weights* weights, void* out, int32_t* stats,
+                       const moe_routing_out* routing, void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st == MOE_OK) st = check_weights(cfg, weights);
+  if (st != MOE_OK) return st;
+  // placeholders for the route check: real pointers come from the workspace
+  static const int32_t dummy_i = 0;
+  static const float dummy_f = 0.f;
+  st = check_route_args(cfg, x, w_router, bias, gumbel_u, &dummy_i, &dummy_f);
+  if (st != MOE_OK) return st;
+  if (cfg->T > 0 && (!out || !aligned16(out))) return fail(MOE_ERR_INVALID_ARGUMENT, "out must be non-NULL and 16-byte aligned");
+  const Layout L = layout_of(cfg);
+  st = check_ws(ws, ws_bytes, L.total);
+  if (st != MOE_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* w = (char*)ws;
+  float* logits = (routing && routing->logits) ? routing->logits : (float*)(w + L.logits);
+  int32_t* idx = (routing && routing->topk_idx) ? routing->topk_idx : (int32_t*)(w + L.idx);
+  float* tw = (routing && routing->topk_w) ? routing->topk_w : (float*)(w + L.w);
+  int32_t* dest = (routing && routing->dest_row) ? routing->dest_row : (int32_t*)(w + L.dest);
+  int32_t* counts = (int32_t*)(w + L.counts);
+  int32_t* offsets = (int32_t*)(w + L.offsets);
+  int32_t* src = (int32_t*)(w + L.src);
+  int32_t* ndrop = (int32_t*)(w + L.ndrop);
+  void* x_perm = w + L.x_perm;
+  float* y_perm = (float*)(w + L.y_perm);
+  float* y_sh = cfg->n_shared ? (float*)(w + L.y_sh) : nullptr;
+
+  st = run_route(cfg, x, w_router, bias, gumbel_u, (routing && routing->logits) ? logits : nullptr, idx, tw, s);
+  if (st != MOE_OK) return st;
+  st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, x_perm, stats, w, s);
+  if (st != MOE_OK) return st;
+  st = run_ffn(cfg, x, x_perm, offsets, weights, y_perm, y_sh, w, s);
+  if (st != MOE_OK) return st;
+  return run_combine(cfg, y_perm, y_sh, dest, tw, out, s);
+}
+
+moe_status moe_profile_enable(int32_t on) {
+  g_prof = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_kernel_time* out, int32_t max_entries, int32_t* n_entries) {
+  g_err[0] = 0;
+  if (!n_entries || (max_entries > 0 && !out)) return fail(MOE_ERR_INVALID_ARGUMENT, "output pointer is NULL");
+  std::vector<moe_kernel_time> acc;
+  for (const ProfRec& r : g_recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.stop) != hipSuccess || hipEventElapsedTime(&ms, r.start, r.stop) != hipSuccess)
+      ms = 0.f;
+    moe_kernel_time* slot = nullptr;
+    for (auto& a : acc)
+      if (std::strncmp(a.name, r.name, sizeof(a.name)) == 0) slot = &a;
+    if (!slot) {
+      moe_kernel_time t{};
+      std::snprintf(t.name, sizeof(t.name), "%s", r.name);
+      acc.push_back(t);
+      slot = &acc.back();
+    }
+    slot->launches += 1;
+    slot->total_ms += ms;
+    g_pool.push_back(r.start);
+    g_pool.push_back(r.stop);
+  }
+  g_recs.clear();
+  const int n = (int)acc.size();
+  for (int i = 0; i < n && i < max_entries; ++i) out[i] = acc[i];
+  *n_entries = n;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,172 @@
+"""GPU parity of every stage of the layer against the oracle, through the C ABI,
+at sizes the oracle finishes in seconds that still span several tiles and
+ragged tails (the full-size workloads are in test_gpu_fullsize.py)."""
+import numpy as np
+import pytest
+import torch
+
+from mixture_experts_sparse_amd import workloads as W
+from oracle import from_inputs as FI
+from oracle import moe_oracle as O
+from tests import gpu_util as G
+
+pytestmark = pytest.mark.gpu
+
+WK = W.WORKLOADS
+SMALL = {
+    "tiny_fp32": WK["tiny_fp32"],
+    "mixtral_small": W.shrink(WK["mixtral_bf16"], T=1000, d=512, F=1024),
+    "gumbel_small": W.shrink(WK["gumbel_bf16"], T=300, d=384, F=256),
+    "fine_shared_small": W.shrink(WK["fine_shared_bf16"], T=150, d=256, F=128),
+    "skewed_fp8_small": W.shrink(WK["skewed_fp8"], T=700, d=256, F=192),
+    "skewed_fp8_decode": WK["skewed_fp8_decode"],
+    "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
+    "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
+    "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
+    "single_token": WK["mixtral_bf16"].replace(name="one", T=1, d=256, E=8, k=2, F=128),
+    "f32_ragged": WK["tiny_fp32"].replace(name="f32r", T=203, d=256, E=6, k=2, F=96),
+}
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch.device("cuda")
+
+
+def _inputs(sh, dev):
+    G.banner(f"{sh.name} T={sh.T} d={sh.d} E={sh.E} k={sh.k} F={sh.F} w={sh.w_dtype}")
+    return W.make_inputs(sh, device=dev)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_stage_parity(name, dev):
+    """Each stage on identical inputs: route, permute (bit-exact), FFN + combine."""
+    sh = SMALL[name]
+    inp = _inputs(sh, dev)
+    g = G.run_stages(inp)
+    rep = {}
+    G.check_routing(inp, g, rep)
+    P = G.check_permutation(sh, g, rep)
+    n = int(P.offsets[-1])
+    x_np = G.to_np(inp.x)
+    # x_perm rows are exact copies of the source tokens
+    assert np.array_equal(g["x_perm"], x_np[P.src_token[:n]])
+    # expert outputs row by row, and the combined output
+    ew = FI.expert_weights(inp)
+    y_ora = O.expert_outputs(x_np[P.src_token[:n]].astype(np.float64), P.offsets, ew)
+    rep["y_err"] = G.out_err(g["y_perm"], y_ora)
+    y_sh = None
+    if sh.n_shared:
+        wg, wu, wd = FI.shared_weights(inp).expert(0)
+        y_sh = O.swiglu_ffn(x_np.astype(np.float64), wg, wu, wd)
+        rep["y_shared_err"] = G.out_err(g["y_shared"], y_sh)
+    out_ora = O.combine(y_ora, P.dest_row, g["topk_w"], y_sh)
+    rep["out_err"] = G.out_err(g["out"], out_ora)
+    print(rep, flush=True)
+    tol = G.TOL_OUT[sh.w_dtype]
+    assert rep["y_err"] <= tol and rep["out_err"] <= tol, rep
+    if sh.n_shared:
+        assert rep["y_shared_err"] <= tol, rep
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_matches_oracle_and_stages(name, dev):
+    """moe_forward end to end against the oracle's own forward; the fused entry
+    point and the four stage entry points give bit-identical results."""
+    sh = SMALL[name]
+    inp = _inputs(sh, dev)
+    f = G.run_forward(inp)
+    s = G.run_stages(inp)
+    for key in ["logits", "topk_idx", "topk_w", "dest_row", "counts", "out"]:
+        assert np.array_equal(f[key], s[key]), key
+    assert f["n_dropped"] == s["n_dropped"]
+    ora = FI.forward(inp)
+    rep = {}
+    sel_tie = ora.routing.gap_sel < G.NEAR_TIE
+    same = np.all(np.sort(ora.routing.idx, 1) == np.sort(f["topk_idx"], 1), axis=1)
+    rep["near_tie_sel"] = int(sel_tie.sum())
+    rep["flips"] = int((~same).sum())
+    assert np.all(same | sel_tie)
+    if rep["flips"] == 0:
+        assert np.array_equal(f["counts"], ora.perm.counts)
+        assert np.array_equal(f["kept"], ora.perm.kept)
+        assert f["n_dropped"] == ora.perm.n_dropped
+        rep["out_err"] = G.out_err(f["out"], ora.out)
+        assert rep["out_err"] <= G.TOL_OUT[sh.w_dtype], rep
+    print(rep, flush=True)
+
+
+def test_forward_is_deterministic(dev):
+    sh = SMALL["skewed_fp8_small"]
+    inp = _inputs(sh, dev)
+    a = G.run_forward(inp)
+    b = G.run_forward(inp)
+    for key in ["logits", "topk_idx", "topk_w", "dest_row", "counts", "kept", "out"]:
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_bf16_output_is_rne_of_f32_output(dev):
+    sh = SMALL["mixtral_small"]
+    inp = _inputs(sh, dev)
+    a = G.run_forward(inp, out_dtype=W.DT_F32)
+    b = G.run_forward(inp, out_dtype=W.DT_BF16)
+    ref = a["out_t"].to(torch.bfloat16)
+    assert torch.equal(b["out_t"], ref)
+
+
+def test_forced_overflow_drops_exactly_T_minus_C(dev):
+    """k=1 and a +1000 logit bias on expert 5: every token picks expert 5, the
+    first C are kept, T - C are dropped and their outputs are exactly zero."""
+    sh = WK["skewed_fp8"].replace(name="overflow", T=500, d=128, E=16, k=1, F=64, capacity_factor=1.0,
+                                  bias_kind="none")
+    inp = _inputs(sh, dev)
+    b = torch.zeros(16, dtype=torch.float32, device=dev)
+    b[5] = 1000.0
+    inp.bias = b
+    f = G.run_forward(inp)
+    C = O.capacity(500, 1, 16, 1.0)
+    assert C == 31
+    assert f["n_dropped"] == 500 - C
+    assert f["counts"][5] == 500 and f["kept"][5] == C and f["kept"].sum() == C
+    assert np.all(f["topk_idx"][:, 0] == 5)
+    assert np.all(f["dest_row"][:C, 0] == np.arange(C)) and np.all(f["dest_row"][C:, 0] == -1)
+    assert np.all(f["out"][C:] == 0.0)
+    np.testing.assert_allclose(f["topk_w"], 1.0)
+
+
+def test_empty_batch(dev):
+    sh = SMALL["mixtral_small"].replace(name="empty", T=0)
+    lib = G.L()
+    inp = W.make_inputs(sh.replace(T=1), device=dev)
+    cfg = lib.make_config(sh)
+    stats = torch.full((2 * sh.E + 1,), 7, dtype=torch.int32, device=dev)
+    out = torch.empty((0, sh.d), dtype=torch.float32, device=dev)
+    ws = lib.alloc_workspace(cfg, dev)
+    lib.moe_forward(cfg, inp.x, inp.w_router, None, None, lib.expert_weights(inp), out, stats, ws)
+    torch.cuda.synchronize()
+    assert torch.all(stats == 0)
+
+
+def test_permute_ignores_out_of_range_ids(dev):
+    """Expert ids outside [0, E) handed to moe_permute are dropped uncounted."""
+    lib = G.L()
+    sh = SMALL["mixtral_small"].replace(name="badids", T=64)
+    cfg = lib.make_config(sh)
+    inp = W.make_inputs(sh, device=dev)
+    idx = torch.randint(0, sh.E, (sh.T, sh.k), dtype=torch.int32, device=dev)
+    idx[3, 0] = -1
+    idx[10, 1] = sh.E + 4
+    R = lib.permuted_rows(cfg)
+    counts = torch.empty(sh.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(sh.E + 1, dtype=torch.int32, device=dev)
+    dest = torch.empty((sh.T, sh.k), dtype=torch.int32, device=dev)
+    src = torch.empty(R, dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    xp = torch.empty((R, sh.d), dtype=inp.x.dtype, device=dev)
+    ws = lib.alloc_workspace(cfg, dev)
+    lib.moe_permute(cfg, inp.x, idx, counts, offsets, dest, src, nd, xp, ws)
+    torch.cuda.synchronize()
+    assert int(counts.sum()) == sh.T * sh.k - 2
+    assert int(dest[3, 0]) == -1 and int(dest[10, 1]) == -1
+    assert int(offsets[-1]) == sh.T * sh.k - 2
