@@ -215,7 +215,7 @@ def main():
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
-        sample = args.cpu_sample or min(sh.T, 256)
+        sample = args.cpu_sample or min(sh.T, 4096)
         print(f"[bench] cpu oracle on {sample} tokens", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, sample)
     else:
