@@ -23,7 +23,9 @@
 // (OCP e4m3fn) codes are converted exactly to bf16 on their way into LDS; the
 // per-output-row scale multiplies the f32 accumulator in the epilogue.
 // fp32 weights: a plain LDS-tiled SIMT kernel (the tiny fp32 workload).
-#include "common.h"
+#include <cstdlib>
+
+#include "grouped.h"
 
 namespace moe {
 namespace {
@@ -69,31 +71,6 @@ __global__ __launch_bounds__(512) void tiles_kernel(const int32_t* __restrict__ 
     goff[i] = o[i];
     tile_prefix[i] = (i == 0) ? 0 : tp[i - 1];
   }
-}
-
-struct TileRef {
-  int g, nt, row0, rows;
-};
-
-// Map a linear tile index to (group, n-tile, first row, valid rows).
-__device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int bm,
-                                            const int32_t* __restrict__ tp,
-                                            const int32_t* __restrict__ goff) {
-  int lo = 0, hi = groups;  // largest g with n_tiles * tp[g] <= L
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)tp[mid] * n_tiles <= L) lo = mid; else hi = mid;
-  }
-  const int g = lo;
-  const int mt = tp[g + 1] - tp[g];
-  const int local = L - tp[g] * n_tiles;
-  const int nt = local / mt, mi = local % mt;
-  TileRef r;
-  r.g = g;
-  r.nt = nt;
-  r.row0 = goff[g] + mi * bm;
-  r.rows = min(bm, goff[g + 1] - r.row0);
-  return r;
 }
 
 struct GemmParams {
@@ -346,9 +323,25 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 
 }  // namespace
 
+// Which kernel runs a pass: the large-tile bf16 kernel when the output width
+// tiles evenly (wave tile 128 x 128, or 128 x 64 for narrower outputs), else the
+// 128 x 128 kernel (fp8, and bf16 shapes the large tiles do not divide), else
+// the fp32 SIMT kernel.
+// returns waves along N of the large-tile kernel (4: 256-wide, 2: 128-wide), or 0
+static int big_waves_n(const GemmLaunch& a) {
+  if (a.w_dtype != MOE_BF16 || a.K % 64) return 0;
+  int pref = 4;
+  if (const char* e = getenv("MOE_GEMM_WAVES_N")) pref = atoi(e);  // experiment knob (removed later)
+  const int width = a.gated ? 32 : 64;  // output columns per wave
+  if (pref == 4 && a.N % (4 * width) == 0) return 4;
+  if (a.N % (2 * width) == 0) return 2;
+  return 0;
+}
+
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   const bool f32 = (a.w_dtype == MOE_F32);
-  const int bm = f32 ? SM : MB;
+  const int wn_big = big_waves_n(a);
+  const int bm = f32 ? SM : (wn_big ? 256 : MB);
   int32_t* goff = a.tile_prefix;
   int32_t* tp = a.tile_prefix + (a.groups + 1);
   int tok = begin_launch("gemm_tiles", s);
@@ -357,6 +350,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   moe_status st = end_launch(tok, s);
   if (st != MOE_OK) return st;
 
+  if (wn_big) return launch_gemm_bf16_big(a, goff, tp, 64, wn_big, s);
   GemmParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
   const int64_t mt_upper = ceil_div(a.max_rows, bm) + a.groups;
   if (f32) {

@@ -1,0 +1,249 @@
+// Grouped bf16 expert GEMM with large tiles for expert groups of hundreds of rows.
+//
+// Same computation and tile walk as gemm.hip (page "MoE sparse activation:
+// principles and engineering practice" (kapook.pages.dev), s4.2 expert fusion;
+// page "GPT-4 has 1.8T parameters but uses 2% per token" (mlqm.cn), s3.3
+// SwiGLU), organised for gfx950's matrix cores:
+//
+//  * block tile 256 rows x (2 WN) weight rows; four waves (2 x 2), each owning a
+//    128 x WN output tile with its accumulators in AGPRs (128 x 128: 256 AGPRs);
+//    LDS bytes read per MFMA are half those of 64 x 64 wave tiles;
+//  * K step 32 per LDS stage, four stages (128 KB at WN = 128): tiles for step
+//    k + 3 are requested while step k runs, by direct global -> LDS loads
+//    (global_load_lds_dwordx4: lane i of a load lands at base + 16 i), so the
+//    prefetch costs no VGPRs;
+//  * LDS rows are 64 bytes with 16-byte chunk c of row r stored at slot
+//    c ^ ((r >> 1) & 3): the 16x16x32 fragment reads (row = lane % 16, chunk =
+//    lane / 16) are then free of bank conflicts.  The swizzle is applied on the
+//    load side by choosing which global chunk each lane fetches;
+//  * B fragments for step k + 1 are read from LDS while the 8 x (WN/16) MFMAs
+//    of step k issue, A fragments stream two at a time; one s_barrier per K
+//    step, waits on the load counter written out explicitly.
+#include <algorithm>
+
+#include "grouped.h"
+
+namespace moe {
+namespace {
+
+#define MOE_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+constexpr int kBK = 32;         // K per stage
+constexpr int kNST = 4;         // LDS stages
+constexpr int kBM = 256;        // rows per block tile
+constexpr int kRow = kBK * 2;   // bytes per LDS row (bf16)
+
+// s_waitcnt immediate: vmcnt(n), no wait on expcnt / lgkmcnt (gfx9 encoding)
+constexpr unsigned vmcnt_imm(int n) { return 0x0F70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
+
+__device__ __forceinline__ void block_sync() {
+  // s_barrier without the memory fence of __syncthreads (which would wait for
+  // every load in flight); the empty asm statements keep the compiler from
+  // moving memory operations across it.
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+struct BigParams {
+  const void* A;
+  const void* B0;
+  const void* B1;
+  void* out;
+  const int32_t* goff;
+  const int32_t* tp;
+  int groups, K, N, n_tiles;
+};
+
+// Waves: 2 along M (128 rows each) x WAVES_N along N (WN weight rows each).
+template <bool GATED, int WN, int WAVES_N>
+__global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigParams p) {
+  constexpr int NW = 2 * WAVES_N;            // waves per block
+  constexpr int BNR = WAVES_N * WN;          // weight rows per block
+  constexpr int A_BYTES = kBM * kRow;        // 16 KB
+  constexpr int B_BYTES = BNR * kRow;
+  constexpr int STAGE = A_BYTES + B_BYTES;
+  constexpr int NJ = WN / 16;                // B fragments per wave
+  constexpr int A_INS = A_BYTES / 1024 / NW; // DMA instructions per wave per stage
+  constexpr int B_INS = B_BYTES / 1024 / NW;
+  constexpr int INS = A_INS + B_INS;
+  static_assert(A_INS * NW * 1024 == A_BYTES && B_INS * NW * 1024 == B_BYTES, "DMA split");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNST * STAGE];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / WAVES_N, wn = w % WAVES_N;
+  const int K = p.K, N = p.N, ksteps = K / kBK;
+  const int total = p.n_tiles * p.tp[p.groups];
+  const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int lend = min(total, (xcd + 1) * chunk);
+  const uint16_t* A = (const uint16_t*)p.A;
+
+  // per-lane constants of the swizzled layout
+  const int dma_row = lane >> 2;                           // row inside a 16-row slab
+  const int dma_chunk = (lane & 3) ^ ((lane >> 3) & 3);    // global chunk this lane fetches
+  const int frow = lane & 15;
+  const int fpos = (lane >> 4) ^ ((frow >> 1) & 3);
+  const uint32_t a_frag = (uint32_t)((wm * 128 + frow) * kRow + fpos * 16);
+  const uint32_t b_frag = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + fpos * 16);
+
+  for (int L = xcd * chunk + jb; L < lend; L += G8) {
+    const TileRef tr = map_tile(L, p.n_tiles, p.groups, kBM, p.tp, p.goff);
+    const int g = tr.g;
+
+    // DMA sources: a wave-uniform base per instruction plus a 32-bit per-lane byte offset
+    const uint8_t* a_base = (const uint8_t*)A + (size_t)tr.row0 * K * 2;
+    uint32_t a_off[A_INS];
+#pragma unroll
+    for (int i = 0; i < A_INS; ++i) {
+      const int r = (w * A_INS + i) * 16 + dma_row;
+      a_off[i] = (uint32_t)((min(r, tr.rows - 1) * K + dma_chunk * 8) * 2);
+    }
+    const uint8_t* b_base[B_INS];
+    uint32_t b_off;
+    {
+      b_off = (uint32_t)((dma_row * K + dma_chunk * 8) * 2);
+#pragma unroll
+      for (int i = 0; i < B_INS; ++i) {
+        const int r0 = (w * B_INS + i) * 16;  // first row of this 16-row slab
+        int wrow0;
+        const void* base;
+        if (GATED) {
+          // wave slab q of wave `half`: WN/2 gate rows then the WN/2 matching up rows;
+          // a 16-row DMA slab is all gate or all up rows
+          const int half = r0 / WN, q = r0 % WN;
+          wrow0 = tr.nt * (BNR / 2) + half * (WN / 2) + (q % (WN / 2));
+          base = (q < WN / 2) ? p.B0 : p.B1;
+        } else {
+          wrow0 = tr.nt * BNR + r0;
+          base = p.B0;
+        }
+        b_base[i] = (const uint8_t*)base + ((size_t)g * N * K + (size_t)wrow0 * K) * 2;
+      }
+    }
+
+    // Loads past the last K step are clamped to the last step: they refill a
+    // buffer no later step reads, and keep the count of loads in flight uniform.
+    auto issue = [&](int ks) {
+      uint8_t* st = smem + (ks % kNST) * STAGE;
+      const uint32_t kb = (uint32_t)min(ks, ksteps - 1) * (kBK * 2);
+#pragma unroll
+      for (int i = 0; i < A_INS; ++i)
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[i] + kb), MOE_LPTR(st + (w * A_INS + i) * 1024),
+                                         16, 0, 0);
+#pragma unroll
+      for (int i = 0; i < B_INS; ++i)
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(b_base[i] + b_off + kb),
+                                         MOE_LPTR(st + A_BYTES + (w * B_INS + i) * 1024), 16, 0, 0);
+    };
+
+    f32x4_t acc[8][NJ];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    bf16x8_t fb[2][NJ];
+
+    block_sync();  // every wave is done with the previous tile's stages
+    issue(0);
+    issue(1);
+    issue(2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * INS));  // step 0 has landed
+    block_sync();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) fb[0][j] = *(const bf16x8_t*)(smem + b_frag + j * 1024);
+
+    // K steps come in pairs (K % 64 == 0), so the B double buffer is indexed statically
+    // and the loop body has no branch around the MFMAs.
+    for (int ks = 0; ks < ksteps; ks += 2) {
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int k = ks + half;
+        const int cur = half, nxt = half ^ 1;
+        const uint8_t* sa = smem + (k % kNST) * STAGE + a_frag;
+        bf16x8_t fa0 = *(const bf16x8_t*)(sa);
+        bf16x8_t fa1 = *(const bf16x8_t*)(sa + 1024);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INS));  // step k + 1 has landed (k + 2 may be in flight)
+        block_sync();
+        issue(k + 3);
+        const uint8_t* sb = smem + ((k + 1) % kNST) * STAGE + b_frag;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) fb[nxt][j] = *(const bf16x8_t*)(sb + j * 1024);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const bf16x8_t fa = (i & 1) ? fa1 : fa0;
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa, fb[cur][j], acc[i][j]);
+          if (i + 2 < 8) {
+            if (i & 1) fa1 = *(const bf16x8_t*)(sa + (i + 2) * 1024);
+            else fa0 = *(const bf16x8_t*)(sa + (i + 2) * 1024);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
+
+    // ---- epilogue (rows past the group's end are not stored)
+    const int col_in = lane & 15;
+    const int rq = (lane >> 4) * 4;
+    if (GATED) {
+      uint16_t* h = (uint16_t*)p.out;
+#pragma unroll
+      for (int j = 0; j < NJ / 2; ++j) {
+        const int f = tr.nt * (BNR / 2) + wn * (WN / 2) + j * 16 + col_in;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = wm * 128 + i * 16 + rq + r;
+            if (m < tr.rows)
+              h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+          }
+      }
+    } else {
+      float* y = (float*)p.out;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) {
+        const int n = tr.nt * BNR + wn * WN + j * 16 + col_in;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int m = wm * 128 + i * 16 + rq + r;
+            if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = acc[i][j][r];
+          }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+// bf16 grouped GEMM with the large-tile kernel: block tile 256 rows x (waves_n * wn)
+// weight rows, 2 x waves_n waves.  Requires N % (gated ? (waves_n * wn / 2) : waves_n * wn) == 0
+// and K % 64 == 0; goff / tile prefix already built for 256-row tiles.
+moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int wn,
+                                int waves_n, hipStream_t s) {
+  BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0};
+  const int bnr = wn * waves_n;
+  p.n_tiles = a.gated ? a.N / (bnr / 2) : a.N / bnr;
+  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles;
+  int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count());
+  grid = ceil_div(grid, 8) * 8;
+  if (grid <= 0) return MOE_OK;
+  const char* name = a.shared ? (a.gated ? "shared_gate_up_bf16" : "shared_down_bf16")
+                              : (a.gated ? "gemm_gate_up_bf16" : "gemm_down_bf16");
+  const dim3 block(128 * waves_n);
+  int tok = begin_launch(name, s);
+  if (waves_n == 4) {
+    if (a.gated) hipLaunchKernelGGL((gemm_bf16_big_kernel<true, 64, 4>), dim3(grid), block, 0, s, p);
+    else hipLaunchKernelGGL((gemm_bf16_big_kernel<false, 64, 4>), dim3(grid), block, 0, s, p);
+  } else {
+    if (a.gated) hipLaunchKernelGGL((gemm_bf16_big_kernel<true, 64, 2>), dim3(grid), block, 0, s, p);
+    else hipLaunchKernelGGL((gemm_bf16_big_kernel<false, 64, 2>), dim3(grid), block, 0, s, p);
+  }
+  return end_launch(tok, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,40 @@
+// Tile walk shared by the grouped GEMM kernels.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+struct TileRef {
+  int g, nt, row0, rows;
+};
+
+// Map a linear tile index L (ordered group-major, then n-tile, then m-tile) to
+// (group, n-tile, first row, valid rows).  tp = exclusive prefix of m-tiles per
+// group, goff = sanitised row offsets; both built by tiles_kernel.
+__device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int bm,
+                                            const int32_t* __restrict__ tp,
+                                            const int32_t* __restrict__ goff) {
+  int lo = 0, hi = groups;  // largest g with n_tiles * tp[g] <= L
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)tp[mid] * n_tiles <= L) lo = mid; else hi = mid;
+  }
+  const int g = lo;
+  const int mt = tp[g + 1] - tp[g];
+  const int local = L - tp[g] * n_tiles;
+  const int nt = local / mt, mi = local % mt;
+  TileRef r;
+  r.g = g;
+  r.nt = nt;
+  r.row0 = goff[g] + mi * bm;
+  r.rows = min(bm, goff[g + 1] - r.row0);
+  return r;
+}
+
+// bf16 large-tile grouped GEMM (gemm_big.hip): wave tile 128 x wn (wn = 64), 2 x waves_n
+// waves (waves_n = 2 or 4), block tile 256 x (waves_n * wn)
+moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int wn,
+                                int waves_n, hipStream_t s);
+
+}  // namespace moe
