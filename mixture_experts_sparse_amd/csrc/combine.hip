@@ -11,10 +11,28 @@
 //
 // Bandwidth-bound: one wave per token, 16-byte vector loads of the k source
 // rows (gathered by dest_row), f32 FMAs in j order, one store of the row.
+// When the down projection split its reduction, the partial sums of a row are
+// added in part order first, so the result does not depend on scheduling.
 #include "common.h"
 
 namespace moe {
 namespace {
+
+struct Parts {
+  const float4* rest;  // parts 1.. of a partial-sum buffer
+  size_t stride4;      // float4s between parts
+  int n;               // number of parts (1 = a plain buffer)
+};
+
+// value of row r, vector v of a buffer that may be split into partial sums
+__device__ __forceinline__ float4 load_parts(const float4* __restrict__ first, const Parts& P, size_t off) {
+  float4 a = first[off];
+  for (int p = 1; p < P.n; ++p) {
+    const float4 b = P.rest[(size_t)(p - 1) * P.stride4 + off];
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  return a;
+}
 
 template <bool BF16OUT>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm,
@@ -22,7 +40,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ topk_w,
                                                       void* __restrict__ out, int T, int vec_per_row,
-                                                      int k, int64_t rows) {
+                                                      int k, int64_t rows, Parts yp, Parts sp) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
@@ -34,14 +52,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
       const int row = dr[j];
       if (row < 0 || row >= rows) continue;  // dropped (or out of range: ignored)
       const float w = wt[j];
-      const float4 y = y_perm[(size_t)row * vec_per_row + v];
+      const float4 y = load_parts(y_perm, yp, (size_t)row * vec_per_row + v);
       acc.x = fmaf(w, y.x, acc.x);
       acc.y = fmaf(w, y.y, acc.y);
       acc.z = fmaf(w, y.z, acc.z);
       acc.w = fmaf(w, y.w, acc.w);
     }
     if (y_shared) {
-      const float4 s = y_shared[(size_t)t * vec_per_row + v];
+      const float4 s = load_parts(y_shared, sp, (size_t)t * vec_per_row + v);
       acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
     }
     if (BF16OUT) {
@@ -61,13 +79,15 @@ moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows) {
   if (a.T == 0) return MOE_OK;
   const int vec = a.d / 4;
   const dim3 grid((unsigned)ceil_div(a.T, 4));
+  const Parts yp{(const float4*)a.y_rest, a.y_stride / 4, a.y_split};
+  const Parts sp{(const float4*)a.sh_rest, a.sh_stride / 4, a.sh_split};
   int tok = begin_launch("combine", s);
   if (a.out_dtype == MOE_BF16)
     hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, (const float4*)a.y_perm,
-                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows);
+                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
   else
     hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, (const float4*)a.y_perm,
-                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows);
+                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
   return end_launch(tok, s);
 }
 

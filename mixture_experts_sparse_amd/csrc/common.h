@@ -98,6 +98,14 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s);
 struct CombineLaunch {
   const float* y_perm; const float* y_shared; const int32_t* dest_row; const float* topk_w;
   void* out; int T, d, k, out_dtype;
+  // y_perm may be the first of y_split partial sums, the others at
+  // y_rest + (p - 1) * y_stride; they are added in order before weighting.
+  int y_split = 1;
+  const float* y_rest = nullptr;
+  size_t y_stride = 0;
+  int sh_split = 1;           // the same for y_shared
+  const float* sh_rest = nullptr;
+  size_t sh_stride = 0;
 };
 // rows: size of y_perm; destinations outside [0, rows) are ignored
 moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows);
@@ -121,7 +129,19 @@ struct GemmLaunch {
   int w_dtype;              // MOE_F32 / MOE_BF16 / MOE_FP8_E4M3FN
   bool gated;
   bool shared;              // the shared expert (names its launches apart)
+  int split_k = 1;          // down pass: K split into parts; part 0 goes to `out`,
+  float* split_rest = nullptr;  // part p >= 1 to split_rest + (p - 1) * split_stride
+  size_t split_stride = 0;  // elements
 };
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+
+// K-split chosen for a down pass of `rows` rows (1 = no split); the large-tile
+// kernel is the only one that splits.  Deterministic function of the shape.
+int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype);
+
+// y[r] += sum_{p = 1 .. split-1} rest[(p-1) * stride + r] for the rows r < offsets[groups]
+// (or < rows when offsets is null), in partial order.
+moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int split,
+                               const int32_t* offsets, int groups, int64_t rows, int d, hipStream_t s);
 
 }  // namespace moe

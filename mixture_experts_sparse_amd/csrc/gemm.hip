@@ -23,6 +23,7 @@
 // (OCP e4m3fn) codes are converted exactly to bf16 on their way into LDS; the
 // per-output-row scale multiplies the f32 accumulator in the epilogue.
 // fp32 weights: a plain LDS-tiled SIMT kernel (the tiny fp32 workload).
+#include <algorithm>
 #include <cstdlib>
 
 #include "grouped.h"
@@ -336,6 +337,58 @@ static int big_waves_n(const GemmLaunch& a) {
   if (pref == 4 && a.N % (4 * width) == 0) return 4;
   if (a.N % (2 * width) == 0) return 2;
   return 0;
+}
+
+int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype) {
+  GemmLaunch probe{};
+  probe.w_dtype = w_dtype;
+  probe.K = K;
+  probe.N = N;
+  probe.gated = false;
+  const int wn = big_waves_n(probe);
+  if (!wn || rows <= 0) return 1;
+  // expected work units: m-tiles (with about half a ragged tile per busy group) x n-tiles x split
+  const int64_t mt = ceil_div(rows, 256);
+  const int64_t est = (mt + std::min<int64_t>(groups, mt) / 2) * (N / (64 * wn));
+  const int cus = device_cu_count();
+  // each extra part costs one more f32 write + read of every row, so a split
+  // must raise the fraction of busy CUs in the last round by 10 points to pay
+  int best = 1;
+  double best_eff = 0.0;
+  for (int sk = 1; sk <= 3; ++sk) {
+    if (K % sk || (K / sk) % 64 || K / sk < 512) continue;
+    const int64_t units = est * sk;
+    const double eff = (double)units / (double)(ceil_div(units, cus) * cus);
+    if (eff > best_eff + 0.10) { best = sk; best_eff = eff; }
+  }
+  return best;
+}
+
+// y[r] += rest parts, for valid rows; one block per 4 rows, float4 lanes
+__global__ __launch_bounds__(256) void sum_partials_kernel(float4* __restrict__ y, const float4* __restrict__ rest,
+                                                           size_t stride4, int split,
+                                                           const int32_t* __restrict__ offsets, int groups,
+                                                           int64_t rows, int vec) {
+  const int64_t n = offsets ? (int64_t)min<int64_t>(offsets[groups], rows) : rows;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  for (int v = threadIdx.x & 63; v < vec; v += 64) {
+    float4 a = y[r * vec + v];
+    for (int p = 1; p < split; ++p) {
+      const float4 b = rest[(size_t)(p - 1) * stride4 + r * vec + v];
+      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+    }
+    y[r * vec + v] = a;
+  }
+}
+
+moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int split, const int32_t* offsets,
+                               int groups, int64_t rows, int d, hipStream_t s) {
+  if (split <= 1 || rows <= 0) return MOE_OK;
+  int tok = begin_launch("sum_partials", s);
+  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, (float4*)y,
+                     (const float4*)rest, stride / 4, split, offsets, groups, rows, d / 4);
+  return end_launch(tok, s);
 }
 
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {

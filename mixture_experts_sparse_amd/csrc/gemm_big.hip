@@ -54,6 +54,9 @@ struct BigParams {
   const int32_t* goff;
   const int32_t* tp;
   int groups, K, N, n_tiles;
+  int split;             // K split into this many parts (down pass only)
+  float* split_rest;     // part p >= 1 goes to split_rest + (p - 1) * split_stride
+  size_t split_stride;
 };
 
 // Waves: 2 along M (128 rows each) x WAVES_N along N (WN weight rows each).
@@ -73,8 +76,10 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w / WAVES_N, wn = w % WAVES_N;
-  const int K = p.K, N = p.N, ksteps = K / kBK;
-  const int total = p.n_tiles * p.tp[p.groups];
+  const int K = p.K, N = p.N;
+  const int kpart = K / p.split, ksteps = kpart / kBK;
+  const int tiles = p.n_tiles * p.tp[p.groups];
+  const int total = tiles * p.split;  // work units: (K part, tile), K part major
   const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int lend = min(total, (xcd + 1) * chunk);
@@ -88,12 +93,14 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
   const uint32_t a_frag = (uint32_t)((wm * 128 + frow) * kRow + fpos * 16);
   const uint32_t b_frag = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + fpos * 16);
 
-  for (int L = xcd * chunk + jb; L < lend; L += G8) {
+  for (int U = xcd * chunk + jb; U < lend; U += G8) {
+    const int part = U / tiles, L = U - part * tiles;
     const TileRef tr = map_tile(L, p.n_tiles, p.groups, kBM, p.tp, p.goff);
     const int g = tr.g;
+    const size_t kofs = (size_t)part * kpart * 2;  // byte offset of this K part
 
     // DMA sources: a wave-uniform base per instruction plus a 32-bit per-lane byte offset
-    const uint8_t* a_base = (const uint8_t*)A + (size_t)tr.row0 * K * 2;
+    const uint8_t* a_base = (const uint8_t*)A + (size_t)tr.row0 * K * 2 + kofs;
     uint32_t a_off[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
@@ -119,7 +126,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
           wrow0 = tr.nt * BNR + r0;
           base = p.B0;
         }
-        b_base[i] = (const uint8_t*)base + ((size_t)g * N * K + (size_t)wrow0 * K) * 2;
+        b_base[i] = (const uint8_t*)base + ((size_t)g * N * K + (size_t)wrow0 * K) * 2 + kofs;
       }
     }
 
@@ -143,7 +150,7 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t fb[2][NJ];
+    bf16x8_t fa[2][8], fb[2][NJ];
 
     block_sync();  // every wave is done with the previous tile's stages
     issue(0);
@@ -152,34 +159,30 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * INS));  // step 0 has landed
     block_sync();
 #pragma unroll
+    for (int i = 0; i < 8; ++i) fa[0][i] = *(const bf16x8_t*)(smem + a_frag + i * 1024);
+#pragma unroll
     for (int j = 0; j < NJ; ++j) fb[0][j] = *(const bf16x8_t*)(smem + b_frag + j * 1024);
 
-    // K steps come in pairs (K % 64 == 0), so the B double buffer is indexed statically
-    // and the loop body has no branch around the MFMAs.
+    // K steps come in pairs (K % 64 == 0), so the fragment double buffer is
+    // indexed statically and the loop body has no branch around the MFMAs.
+    // The fragments of step k + 1 are read while the MFMAs of step k issue.
     for (int ks = 0; ks < ksteps; ks += 2) {
 #pragma unroll
       for (int half = 0; half < 2; ++half) {
         const int k = ks + half;
         const int cur = half, nxt = half ^ 1;
-        const uint8_t* sa = smem + (k % kNST) * STAGE + a_frag;
-        bf16x8_t fa0 = *(const bf16x8_t*)(sa);
-        bf16x8_t fa1 = *(const bf16x8_t*)(sa + 1024);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(INS));  // step k + 1 has landed (k + 2 may be in flight)
         block_sync();
         issue(k + 3);
-        const uint8_t* sb = smem + ((k + 1) % kNST) * STAGE + b_frag;
+        const uint8_t* sn = smem + ((k + 1) % kNST) * STAGE;
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) fb[nxt][j] = *(const bf16x8_t*)(sb + j * 1024);
+        for (int i = 0; i < 8; ++i) fa[nxt][i] = *(const bf16x8_t*)(sn + a_frag + i * 1024);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const bf16x8_t fa = (i & 1) ? fa1 : fa0;
+        for (int j = 0; j < NJ; ++j) fb[nxt][j] = *(const bf16x8_t*)(sn + b_frag + j * 1024);
 #pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa, fb[cur][j], acc[i][j]);
-          if (i + 2 < 8) {
-            if (i & 1) fa1 = *(const bf16x8_t*)(sa + (i + 2) * 1024);
-            else fa0 = *(const bf16x8_t*)(sa + (i + 2) * 1024);
-          }
-        }
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa[cur][i], fb[cur][j], acc[i][j]);
       }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
@@ -188,21 +191,37 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
     const int col_in = lane & 15;
     const int rq = (lane >> 4) * 4;
     if (GATED) {
-      uint16_t* h = (uint16_t*)p.out;
+      // h = silu(g) * u for this wave's 128 rows x WN/2 columns, staged through
+      // LDS (stages are free: every wave has passed its last MFMA once all
+      // waves reach the barrier) and stored as 16-byte row segments.
+      constexpr int HC = WN / 2;                      // h columns per wave
+      constexpr int HROW = HC * 2;                    // bytes per staged row
+      uint8_t* hs = smem + w * (128 * HROW);
+      block_sync();
 #pragma unroll
-      for (int j = 0; j < NJ / 2; ++j) {
-        const int f = tr.nt * (BNR / 2) + wn * (WN / 2) + j * 16 + col_in;
+      for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int m = wm * 128 + i * 16 + rq + r;
-            if (m < tr.rows)
-              h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+            const int m = i * 16 + rq + r;
+            const uint16_t hv = f32_to_bf16_rne(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+            *(uint16_t*)(hs + m * HROW + (j * 16 + col_in) * 2) = hv;
           }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged h visible to the wave
+      uint16_t* h = (uint16_t*)p.out;
+      constexpr int SEG = HROW / 16;                  // 16-byte segments per row
+      const int f0 = tr.nt * (BNR / 2) + wn * HC;
+#pragma unroll
+      for (int it = 0; it < 128 * SEG / 64; ++it) {
+        const int idx = it * 64 + lane;
+        const int m = idx / SEG, sg = idx % SEG;
+        const uint4 v = *(const uint4*)(hs + m * HROW + sg * 16);
+        if (wm * 128 + m < tr.rows)
+          *(uint4*)(h + (size_t)(tr.row0 + wm * 128 + m) * N + f0 + sg * 8) = v;
       }
     } else {
-      float* y = (float*)p.out;
+      float* y = part == 0 ? (float*)p.out : p.split_rest + (size_t)(part - 1) * p.split_stride;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int n = tr.nt * BNR + wn * WN + j * 16 + col_in;
@@ -225,10 +244,11 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
 // and K % 64 == 0; goff / tile prefix already built for 256-row tiles.
 moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int wn,
                                 int waves_n, hipStream_t s) {
-  BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0};
+  BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gated ? 1 : a.split_k,
+              a.split_rest, a.split_stride};
   const int bnr = wn * waves_n;
   p.n_tiles = a.gated ? a.N / (bnr / 2) : a.N / bnr;
-  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles;
+  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles * p.split;
   int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count());
   grid = ceil_div(grid, 8) * 8;
   if (grid <= 0) return MOE_OK;
