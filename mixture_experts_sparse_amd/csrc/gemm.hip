@@ -24,7 +24,6 @@
 // per-output-row scale multiplies the f32 accumulator in the epilogue.
 // fp32 weights: a plain LDS-tiled SIMT kernel (the tiny fp32 workload).
 #include <algorithm>
-#include <cstdlib>
 
 #include "grouped.h"
 
@@ -328,15 +327,10 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // tiles evenly (wave tile 128 x 128, or 128 x 64 for narrower outputs), else the
 // 128 x 128 kernel (fp8, and bf16 shapes the large tiles do not divide), else
 // the fp32 SIMT kernel.
-// returns waves along N of the large-tile kernel (4: 256-wide, 2: 128-wide), or 0
-static int big_waves_n(const GemmLaunch& a) {
-  if (a.w_dtype != MOE_BF16 || a.K % 64) return 0;
-  int pref = 4;
-  if (const char* e = getenv("MOE_GEMM_WAVES_N")) pref = atoi(e);  // experiment knob (removed later)
-  const int width = a.gated ? 32 : 64;  // output columns per wave
-  if (pref == 4 && a.N % (4 * width) == 0) return 4;
-  if (a.N % (2 * width) == 0) return 2;
-  return 0;
+// whether the large-tile bf16 kernel (256 x 256 block tiles) runs this pass
+static bool use_big(const GemmLaunch& a) {
+  if (a.w_dtype != MOE_BF16 || a.K % 64) return false;
+  return a.gated ? (a.N % 128 == 0) : (a.N % 256 == 0);
 }
 
 int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype) {
@@ -345,21 +339,20 @@ int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype) {
   probe.K = K;
   probe.N = N;
   probe.gated = false;
-  const int wn = big_waves_n(probe);
-  if (!wn || rows <= 0) return 1;
+  if (!use_big(probe) || rows <= 0) return 1;
   // expected work units: m-tiles (with about half a ragged tile per busy group) x n-tiles x split
   const int64_t mt = ceil_div(rows, 256);
-  const int64_t est = (mt + std::min<int64_t>(groups, mt) / 2) * (N / (64 * wn));
+  const int64_t est = (mt + std::min<int64_t>(groups, mt) / 2) * (N / 256);
   const int cus = device_cu_count();
   // each extra part costs one more f32 write + read of every row, so a split
-  // must raise the fraction of busy CUs in the last round by 10 points to pay
+  // must raise the share of CU-rounds doing work by 15 % to be taken
   int best = 1;
   double best_eff = 0.0;
   for (int sk = 1; sk <= 3; ++sk) {
     if (K % sk || (K / sk) % 64 || K / sk < 512) continue;
     const int64_t units = est * sk;
     const double eff = (double)units / (double)(ceil_div(units, cus) * cus);
-    if (eff > best_eff + 0.10) { best = sk; best_eff = eff; }
+    if (eff > best_eff * 1.15) { best = sk; best_eff = eff; }
   }
   return best;
 }
@@ -393,8 +386,8 @@ moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int s
 
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   const bool f32 = (a.w_dtype == MOE_F32);
-  const int wn_big = big_waves_n(a);
-  const int bm = f32 ? SM : (wn_big ? 256 : MB);
+  const bool big = use_big(a);
+  const int bm = f32 ? SM : (big ? 256 : MB);
   int32_t* goff = a.tile_prefix;
   int32_t* tp = a.tile_prefix + (a.groups + 1);
   int tok = begin_launch("gemm_tiles", s);
@@ -403,7 +396,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   moe_status st = end_launch(tok, s);
   if (st != MOE_OK) return st;
 
-  if (wn_big) return launch_gemm_bf16_big(a, goff, tp, 64, wn_big, s);
+  if (big) return launch_gemm_bf16_big(a, goff, tp, s);
   GemmParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
   const int64_t mt_upper = ceil_div(a.max_rows, bm) + a.groups;
   if (f32) {

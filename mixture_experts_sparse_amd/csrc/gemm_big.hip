@@ -8,17 +8,21 @@
 //  * block tile 256 rows x (2 WN) weight rows; four waves (2 x 2), each owning a
 //    128 x WN output tile with its accumulators in AGPRs (128 x 128: 256 AGPRs);
 //    LDS bytes read per MFMA are half those of 64 x 64 wave tiles;
-//  * K step 32 per LDS stage, four stages (128 KB at WN = 128): tiles for step
-//    k + 3 are requested while step k runs, by direct global -> LDS loads
+//  * K step 64 per LDS stage (128-byte rows: every fetch is a whole cache
+//    line), two stages of 64 KB, filled by direct global -> LDS loads
 //    (global_load_lds_dwordx4: lane i of a load lands at base + 16 i), so the
 //    prefetch costs no VGPRs;
-//  * LDS rows are 64 bytes with 16-byte chunk c of row r stored at slot
-//    c ^ ((r >> 1) & 3): the 16x16x32 fragment reads (row = lane % 16, chunk =
-//    lane / 16) are then free of bank conflicts.  The swizzle is applied on the
-//    load side by choosing which global chunk each lane fetches;
-//  * B fragments for step k + 1 are read from LDS while the 8 x (WN/16) MFMAs
-//    of step k issue, A fragments stream two at a time; one s_barrier per K
-//    step, waits on the load counter written out explicitly.
+//  * 16-byte chunk c of row r is stored at slot c ^ (r & 7): the 16x16x32
+//    fragment reads (row = lane % 16, chunk = lane / 16 (+4)) are then free of
+//    bank conflicts.  The swizzle is applied on the load side by choosing
+//    which global chunk each lane fetches;
+//  * each K step is two 32-wide halves with their own fragment registers: the
+//    fragments of one half are read while the MFMAs of the other issue; the
+//    single s_barrier of a step sits between the halves, after which the
+//    step-after-next is requested into the stage just consumed;
+//  * the eight load instructions and the fragment reads of a half are spread
+//    one per MFMA row (scheduling barriers keep that order), so the memory
+//    pipeline never receives a burst that would stall MFMA issue.
 #include <algorithm>
 
 #include "grouped.h"
@@ -29,13 +33,13 @@ namespace {
 #define MOE_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
-constexpr int kBK = 32;         // K per stage
-constexpr int kNST = 4;         // LDS stages
+constexpr int kBK = 64;         // K per stage
 constexpr int kBM = 256;        // rows per block tile
 constexpr int kRow = kBK * 2;   // bytes per LDS row (bf16)
 
-// s_waitcnt immediate: vmcnt(n), no wait on expcnt / lgkmcnt (gfx9 encoding)
+// s_waitcnt immediates (gfx9 encoding): vmcnt(n) alone, and lgkmcnt(0) alone
 constexpr unsigned vmcnt_imm(int n) { return 0x0F70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
+constexpr unsigned kLgkm0 = 0xC07Fu;
 
 __device__ __forceinline__ void block_sync() {
   // s_barrier without the memory fence of __syncthreads (which would wait for
@@ -59,22 +63,22 @@ struct BigParams {
   size_t split_stride;
 };
 
-// Waves: 2 along M (128 rows each) x WAVES_N along N (WN weight rows each).
-template <bool GATED, int WN, int WAVES_N>
-__global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigParams p) {
-  constexpr int NW = 2 * WAVES_N;            // waves per block
-  constexpr int BNR = WAVES_N * WN;          // weight rows per block
-  constexpr int A_BYTES = kBM * kRow;        // 16 KB
-  constexpr int B_BYTES = BNR * kRow;
-  constexpr int STAGE = A_BYTES + B_BYTES;
+// Waves: 2 along M (128 rows each) x 4 along N (64 weight rows each).
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
+  constexpr int WN = 64, WAVES_N = 4, NW = 8;
+  constexpr int BNR = WAVES_N * WN;          // 256 weight rows per block
+  constexpr int A_BYTES = kBM * kRow;        // 32 KB
+  constexpr int B_BYTES = BNR * kRow;        // 32 KB
+  constexpr int STAGE = A_BYTES + B_BYTES;   // 64 KB; two stages
   constexpr int NJ = WN / 16;                // B fragments per wave
-  constexpr int A_INS = A_BYTES / 1024 / NW; // DMA instructions per wave per stage
-  constexpr int B_INS = B_BYTES / 1024 / NW;
-  constexpr int INS = A_INS + B_INS;
-  static_assert(A_INS * NW * 1024 == A_BYTES && B_INS * NW * 1024 == B_BYTES, "DMA split");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[kNST * STAGE];
+  constexpr int A_INS = A_BYTES / 1024 / NW; // 4 DMA instructions (8 rows each) per wave
+  constexpr int B_INS = B_BYTES / 1024 / NW; // 4
+  static_assert(A_INS + B_INS == 8, "one load per MFMA row");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int wm = w / WAVES_N, wn = w % WAVES_N;
   const int K = p.K, N = p.N;
   const int kpart = K / p.split, ksteps = kpart / kBK;
@@ -83,15 +87,16 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
   const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
   const int chunk = (total + 7) >> 3;
   const int lend = min(total, (xcd + 1) * chunk);
-  const uint16_t* A = (const uint16_t*)p.A;
 
   // per-lane constants of the swizzled layout
-  const int dma_row = lane >> 2;                           // row inside a 16-row slab
-  const int dma_chunk = (lane & 3) ^ ((lane >> 3) & 3);    // global chunk this lane fetches
+  const int dma_row = lane >> 3;                  // row inside an 8-row slab
+  const int dma_chunk = (lane & 7) ^ dma_row;     // global 16-byte chunk this lane fetches
   const int frow = lane & 15;
-  const int fpos = (lane >> 4) ^ ((frow >> 1) & 3);
-  const uint32_t a_frag = (uint32_t)((wm * 128 + frow) * kRow + fpos * 16);
-  const uint32_t b_frag = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + fpos * 16);
+  const int kg = lane >> 4;                       // k group of the fragment (8 values each)
+  const uint32_t a_frag0 = (uint32_t)((wm * 128 + frow) * kRow + ((kg ^ (frow & 7)) * 16));
+  const uint32_t a_frag1 = (uint32_t)((wm * 128 + frow) * kRow + (((kg + 4) ^ (frow & 7)) * 16));
+  const uint32_t b_frag0 = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + ((kg ^ (frow & 7)) * 16));
+  const uint32_t b_frag1 = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + (((kg + 4) ^ (frow & 7)) * 16));
 
   for (int U = xcd * chunk + jb; U < lend; U += G8) {
     const int part = U / tiles, L = U - part * tiles;
@@ -99,50 +104,43 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
     const int g = tr.g;
     const size_t kofs = (size_t)part * kpart * 2;  // byte offset of this K part
 
-    // DMA sources: a wave-uniform base per instruction plus a 32-bit per-lane byte offset
-    const uint8_t* a_base = (const uint8_t*)A + (size_t)tr.row0 * K * 2 + kofs;
+    // load sources: wave-uniform bases plus 32-bit per-lane byte offsets
+    const uint8_t* a_base = (const uint8_t*)p.A + (size_t)tr.row0 * K * 2 + kofs;
     uint32_t a_off[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-      const int r = (w * A_INS + i) * 16 + dma_row;
+      const int r = (w * A_INS + i) * 8 + dma_row;
       a_off[i] = (uint32_t)((min(r, tr.rows - 1) * K + dma_chunk * 8) * 2);
     }
+    const uint32_t b_off = (uint32_t)((dma_row * K + dma_chunk * 8) * 2);
     const uint8_t* b_base[B_INS];
-    uint32_t b_off;
-    {
-      b_off = (uint32_t)((dma_row * K + dma_chunk * 8) * 2);
 #pragma unroll
-      for (int i = 0; i < B_INS; ++i) {
-        const int r0 = (w * B_INS + i) * 16;  // first row of this 16-row slab
-        int wrow0;
-        const void* base;
-        if (GATED) {
-          // wave slab q of wave `half`: WN/2 gate rows then the WN/2 matching up rows;
-          // a 16-row DMA slab is all gate or all up rows
-          const int half = r0 / WN, q = r0 % WN;
-          wrow0 = tr.nt * (BNR / 2) + half * (WN / 2) + (q % (WN / 2));
-          base = (q < WN / 2) ? p.B0 : p.B1;
-        } else {
-          wrow0 = tr.nt * BNR + r0;
-          base = p.B0;
-        }
-        b_base[i] = (const uint8_t*)base + ((size_t)g * N * K + (size_t)wrow0 * K) * 2 + kofs;
+    for (int i = 0; i < B_INS; ++i) {
+      const int r0 = (w * B_INS + i) * 8;  // first row of this 8-row slab
+      int wrow0;
+      const void* base;
+      if (GATED) {
+        // wave slab `half`: WN/2 gate rows then the WN/2 matching up rows
+        const int half = r0 / WN, q = r0 % WN;
+        wrow0 = tr.nt * (BNR / 2) + half * (WN / 2) + (q % (WN / 2));
+        base = (q < WN / 2) ? p.B0 : p.B1;
+      } else {
+        wrow0 = tr.nt * BNR + r0;
+        base = p.B0;
       }
+      b_base[i] = (const uint8_t*)base + ((size_t)g * N * K + (size_t)wrow0 * K) * 2 + kofs;
     }
-
-    // Loads past the last K step are clamped to the last step: they refill a
-    // buffer no later step reads, and keep the count of loads in flight uniform.
-    auto issue = [&](int ks) {
-      uint8_t* st = smem + (ks % kNST) * STAGE;
-      const uint32_t kb = (uint32_t)min(ks, ksteps - 1) * (kBK * 2);
-#pragma unroll
-      for (int i = 0; i < A_INS; ++i)
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[i] + kb), MOE_LPTR(st + (w * A_INS + i) * 1024),
+    // load instruction q (0..7) of step ks; steps past the last are clamped to
+    // it (they refill the stage just consumed, which no later step reads)
+    auto load_one = [&](int q, int ks) {
+      uint8_t* st = smem + (ks & 1) * STAGE;
+      const uint32_t kb = (uint32_t)min(ks, ksteps - 1) * kRow;
+      if (q < A_INS)
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[q] + kb), MOE_LPTR(st + (w * A_INS + q) * 1024),
                                          16, 0, 0);
-#pragma unroll
-      for (int i = 0; i < B_INS; ++i)
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(b_base[i] + b_off + kb),
-                                         MOE_LPTR(st + A_BYTES + (w * B_INS + i) * 1024), 16, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(b_base[q - A_INS] + b_off + kb),
+                                         MOE_LPTR(st + A_BYTES + (w * B_INS + q - A_INS) * 1024), 16, 0, 0);
     };
 
     f32x4_t acc[8][NJ];
@@ -150,42 +148,48 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
     for (int i = 0; i < 8; ++i)
 #pragma unroll
       for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    bf16x8_t fa[2][8], fb[2][NJ];
+    bf16x8_t X[8 + NJ], Y[8 + NJ];  // fragments of the first / second 32-wide half of a step
 
-    block_sync();  // every wave is done with the previous tile's stages
-    issue(0);
-    issue(1);
-    issue(2);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * INS));  // step 0 has landed
+    block_sync();  // every wave is done with the previous unit's stages
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load_one(q, 0);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) load_one(q, 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));  // step 0 has landed
     block_sync();
 #pragma unroll
-    for (int i = 0; i < 8; ++i) fa[0][i] = *(const bf16x8_t*)(smem + a_frag + i * 1024);
+    for (int i = 0; i < 8; ++i) X[i] = *(const bf16x8_t*)(smem + a_frag0 + i * 2048);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) fb[0][j] = *(const bf16x8_t*)(smem + b_frag + j * 1024);
+    for (int j = 0; j < NJ; ++j) X[8 + j] = *(const bf16x8_t*)(smem + b_frag0 + j * 2048);
 
-    // K steps come in pairs (K % 64 == 0), so the fragment double buffer is
-    // indexed statically and the loop body has no branch around the MFMAs.
-    // The fragments of step k + 1 are read while the MFMAs of step k issue.
-    for (int ks = 0; ks < ksteps; ks += 2) {
+    for (int ks = 0; ks < ksteps; ++ks) {
+      const uint8_t* sc = smem + (ks & 1) * STAGE;
+      const uint8_t* sn = smem + ((ks + 1) & 1) * STAGE;
+      // first half: MFMAs on X, second-half fragments of this step read alongside
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int k = ks + half;
-        const int cur = half, nxt = half ^ 1;
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(INS));  // step k + 1 has landed (k + 2 may be in flight)
-        block_sync();
-        issue(k + 3);
-        const uint8_t* sn = smem + ((k + 1) % kNST) * STAGE;
+      for (int i = 0; i < 8; ++i) {
+        Y[i] = *(const bf16x8_t*)(sc + a_frag1 + i * 2048);
+        if (i < NJ) Y[8 + i] = *(const bf16x8_t*)(sc + b_frag1 + i * 2048);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) fa[nxt][i] = *(const bf16x8_t*)(sn + a_frag + i * 1024);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[i], X[8 + j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // step ks + 1 has landed
+      __builtin_amdgcn_s_waitcnt(kLgkm0);         // this wave's reads of step ks are done
+      block_sync();
+      // second half: MFMAs on Y; step ks + 2 requested into this step's stage and
+      // the first-half fragments of step ks + 1 read, one of each per MFMA row
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) fb[nxt][j] = *(const bf16x8_t*)(sn + b_frag + j * 1024);
+      for (int i = 0; i < 8; ++i) {
+        load_one(i, ks + 2);
+        X[i] = *(const bf16x8_t*)(sn + a_frag0 + i * 2048);
+        if (i < NJ) X[8 + i] = *(const bf16x8_t*)(sn + b_frag0 + i * 2048);
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(fa[cur][i], fb[cur][j], acc[i][j]);
+        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[i], Y[8 + j], acc[i][j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this unit
 
     // ---- epilogue (rows past the group's end are not stored)
     const int col_in = lane & 15;
@@ -239,30 +243,22 @@ __global__ __launch_bounds__(128 * WAVES_N, 1) void gemm_bf16_big_kernel(BigPara
 
 }  // namespace
 
-// bf16 grouped GEMM with the large-tile kernel: block tile 256 rows x (waves_n * wn)
-// weight rows, 2 x waves_n waves.  Requires N % (gated ? (waves_n * wn / 2) : waves_n * wn) == 0
-// and K % 64 == 0; goff / tile prefix already built for 256-row tiles.
-moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int wn,
-                                int waves_n, hipStream_t s) {
+// bf16 grouped GEMM with the large-tile kernel: block tile 256 rows x 256 weight rows,
+// 8 waves.  Requires N % (gated ? 128 : 256) == 0 and K % 64 == 0 (per K part);
+// goff / tile prefix already built for 256-row tiles.
+moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s) {
   BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gated ? 1 : a.split_k,
               a.split_rest, a.split_stride};
-  const int bnr = wn * waves_n;
-  p.n_tiles = a.gated ? a.N / (bnr / 2) : a.N / bnr;
+  p.n_tiles = a.gated ? a.N / 128 : a.N / 256;
   const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles * p.split;
   int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count());
   grid = ceil_div(grid, 8) * 8;
   if (grid <= 0) return MOE_OK;
   const char* name = a.shared ? (a.gated ? "shared_gate_up_bf16" : "shared_down_bf16")
                               : (a.gated ? "gemm_gate_up_bf16" : "gemm_down_bf16");
-  const dim3 block(128 * waves_n);
   int tok = begin_launch(name, s);
-  if (waves_n == 4) {
-    if (a.gated) hipLaunchKernelGGL((gemm_bf16_big_kernel<true, 64, 4>), dim3(grid), block, 0, s, p);
-    else hipLaunchKernelGGL((gemm_bf16_big_kernel<false, 64, 4>), dim3(grid), block, 0, s, p);
-  } else {
-    if (a.gated) hipLaunchKernelGGL((gemm_bf16_big_kernel<true, 64, 2>), dim3(grid), block, 0, s, p);
-    else hipLaunchKernelGGL((gemm_bf16_big_kernel<false, 64, 2>), dim3(grid), block, 0, s, p);
-  }
+  if (a.gated) hipLaunchKernelGGL(gemm_bf16_big_kernel<true>, dim3(grid), dim3(512), 0, s, p);
+  else hipLaunchKernelGGL(gemm_bf16_big_kernel<false>, dim3(grid), dim3(512), 0, s, p);
   return end_launch(tok, s);
 }
 

@@ -32,9 +32,7 @@ __device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int 
   return r;
 }
 
-// bf16 large-tile grouped GEMM (gemm_big.hip): wave tile 128 x wn (wn = 64), 2 x waves_n
-// waves (waves_n = 2 or 4), block tile 256 x (waves_n * wn)
-moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int wn,
-                                int waves_n, hipStream_t s);
+// bf16 large-tile grouped GEMM (gemm_big.hip): block tile 256 x 256, 8 waves of 128 x 64
+moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s);
 
 }  // namespace moe
