@@ -126,10 +126,11 @@ const char* moe_last_error(void);
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 int32_t moe_version(void);
 
-/* Device workspace, in bytes, that moe_permute / moe_expert_ffn / moe_forward
- * need for `cfg` (each entry point needs at most this much).  The pointer
- * passed as `ws` must be 256-byte aligned.  Returns a status; *bytes is set
- * only on MOE_OK. */
+/* Device workspace, in bytes, that moe_route / moe_permute / moe_expert_ffn /
+ * moe_forward need for `cfg` on the current device (each entry point needs at
+ * most this much; the split of the work across compute units, and so the size,
+ * depends on the device).  The pointer passed as `ws` must be 256-byte aligned.
+ * Returns a status; *bytes is set only on MOE_OK. */
 moe_status moe_workspace_bytes(const moe_config* cfg, size_t* bytes);
 
 /* Rows of the permuted buffers (x_perm, y_perm, src_token) the caller must
@@ -145,10 +146,13 @@ moe_status moe_permuted_rows(const moe_config* cfg, int64_t* rows);
  *              ([P2] s5.1); softmax only.  Noise g = -log(-log u) is added to the
  *              (biased) logits before the temperature: l = (z + b + g) / tau.
  *   logits     [T,E] f32 output z, or NULL
- *   topk_idx   [T,k] int32 output;  topk_w [T,k] f32 output */
+ *   topk_idx   [T,k] int32 output;  topk_w [T,k] f32 output
+ *   ws, ws_bytes  device workspace (bf16 x: split router weights and logit
+ *              partials; fp32 x needs none and may pass NULL) */
 moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router,
                      const float* bias, const float* gumbel_u, float* logits,
-                     int32_t* topk_idx, float* topk_w, void* stream);
+                     int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+                     void* stream);
 
 /* Steps 3-4: capacity and permutation ([P2] s3.2; [P3] s4.2; [P5] dynamic
  * routing -- the tensor reorganised by routing index).  Pairs (t,j) are ranked

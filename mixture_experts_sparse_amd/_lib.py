@@ -68,7 +68,7 @@ def _load() -> ctypes.CDLL:
         "moe_version": ([], ctypes.c_int32),
         "moe_workspace_bytes": ([cfgp, ctypes.POINTER(ctypes.c_size_t)], ctypes.c_int),
         "moe_permuted_rows": ([cfgp, ctypes.POINTER(ctypes.c_int64)], ctypes.c_int),
-        "moe_route": ([cfgp, P, P, P, P, P, P, P, P], ctypes.c_int),
+        "moe_route": ([cfgp, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
         "moe_permute": ([cfgp, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
         "moe_expert_ffn": ([cfgp, P, P, P, ctypes.POINTER(moe_expert_weights), P, P, P,
                             ctypes.c_size_t, P], ctypes.c_int),
@@ -145,9 +145,10 @@ def expert_weights(inp: W.MoEInputs) -> moe_expert_weights:
 
 
 # ------------------------------------------------------------------ entry points
-def moe_route(cfg, x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, stream=None):
+def moe_route(cfg, x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, ws, stream=None):
     _check(_LIB.moe_route(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(gumbel_u),
-                          _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _stream(stream)), "moe_route")
+                          _ptr(logits), _ptr(topk_idx), _ptr(topk_w), _ptr(ws),
+                          ws.numel() if ws is not None else 0, _stream(stream)), "moe_route")
 
 
 def moe_permute(cfg, x, topk_idx, counts, offsets, dest_row, src_token, n_dropped, x_perm, ws,

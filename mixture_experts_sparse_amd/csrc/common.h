@@ -78,8 +78,15 @@ struct RouteLaunch {
   float* logits; int32_t* topk_idx; float* topk_w;
   int T, d, E, k, score, renormalize, bias_mode, act_dtype;
   float tau;
+  // bf16 path: padded expert count, d-split, and workspace buffers
+  int ep = 0, split = 0;
+  uint16_t* wt = nullptr;   // [3][ep][d] split router weights
+  float* part = nullptr;    // [split][T][ep] logit partials
 };
 moe_status launch_route(const RouteLaunch& a, hipStream_t s);
+// Router geometry for bf16 activations (ep = 0 for the fp32 path): padded expert
+// count (16 .. 256) and the number of d-slices.  Depends on the device's CU count.
+void route_plan(int T, int d, int E, int act_dtype, int* ep, int* split);
 
 // Permutation geometry: pairs are processed in chunks of kPermChunk.
 constexpr int kPermChunk = 1024;

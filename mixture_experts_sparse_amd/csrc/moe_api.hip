@@ -1,5 +1,6 @@
 // C-ABI entry points of the MoE layer: host-side validation, workspace
 // carving and launch sequencing.  See include/moe.h for the contract.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -140,6 +141,10 @@ int64_t perm_rows(const moe_config* c) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 struct Layout {
+  // router scratch (bf16 path): split weights, logit partials; overlaps the
+  // permute / ffn scratch, which is only used after the router has finished
+  int route_ep, route_split;
+  size_t route_wt, route_part, route_end;
   // permute / ffn scratch
   size_t hist, tiles, tiles_sh, h, h_sh;
   int split, split_sh;          // K splits of the routed / shared down passes
@@ -161,6 +166,11 @@ Layout layout_of(const moe_config* c) {
     o = align_up(o + bytes, 256);
     return at;
   };
+  route_plan(c->T, c->d, c->E, c->act_dtype, &L.route_ep, &L.route_split);
+  L.route_wt = take(sizeof(uint16_t) * 3 * (size_t)L.route_ep * c->d);
+  L.route_part = take(sizeof(float) * (size_t)L.route_split * c->T * L.route_ep);
+  L.route_end = o;
+  o = 0;
   // scratch shared by moe_permute and moe_expert_ffn (they never run concurrently
   // on one workspace within moe_forward; standalone callers pass one each)
   L.hist = take(sizeof(int32_t) * nblk * c->E);
@@ -174,6 +184,7 @@ Layout layout_of(const moe_config* c) {
   L.y_rest = take(sizeof(float) * (size_t)(L.split - 1) * R * c->d);
   L.y_sh_rest = take(sizeof(float) * (size_t)(L.split_sh - 1) * c->T * c->d);
   L.ffn_end = o;
+  o = std::max(L.ffn_end, L.route_end);
   L.logits = take(sizeof(float) * (size_t)c->T * c->E);
   L.idx = take(sizeof(int32_t) * P);
   L.w = take(sizeof(float) * P);
@@ -232,9 +243,15 @@ moe_status check_route_args(const moe_config* c, const void* x, const float* w_r
 
 // ---- step runners shared by the standalone entry points and moe_forward
 moe_status run_route(const moe_config* c, const void* x, const float* w_router, const float* bias,
-                     const float* gumbel_u, float* logits, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+                     const float* gumbel_u, float* logits, int32_t* topk_idx, float* topk_w, char* ws,
+                     hipStream_t s) {
   RouteLaunch r{x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, c->T, c->d, c->E, c->top_k,
                 c->score, c->renormalize, c->bias_mode, c->act_dtype, c->tau};
+  const Layout L = layout_of(c);
+  r.ep = L.route_ep;
+  r.split = L.route_split;
+  r.wt = (uint16_t*)(ws + L.route_wt);
+  r.part = (float*)(ws + L.route_part);
   return launch_route(r, s);
 }
 
@@ -348,12 +365,17 @@ moe_status moe_permuted_rows(const moe_config* cfg, int64_t* rows) {
 }
 
 moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
-                     const float* gumbel_u, float* logits, int32_t* topk_idx, float* topk_w, void* stream) {
+                     const float* gumbel_u, float* logits, int32_t* topk_idx, float* topk_w, void* ws,
+                     size_t ws_bytes, void* stream) {
   g_err[0] = 0;
   moe_status st = check_config(cfg);
   if (st == MOE_OK) st = check_route_args(cfg, x, w_router, bias, gumbel_u, topk_idx, topk_w);
   if (st != MOE_OK) return st;
-  return run_route(cfg, x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, (hipStream_t)stream);
+  if (cfg->T > 0) {
+    st = check_ws(ws, ws_bytes, layout_of(cfg).route_end);
+    if (st != MOE_OK) return st;
+  }
+  return run_route(cfg, x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, (char*)ws, (hipStream_t)stream);
 }
 
 moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx, int32_t* counts,
@@ -436,7 +458,7 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
   float* y_perm = (float*)(w + L.y_perm);
   float* y_sh = cfg->n_shared ? (float*)(w + L.y_sh) : nullptr;
 
-  st = run_route(cfg, x, w_router, bias, gumbel_u, (routing && routing->logits) ? logits : nullptr, idx, tw, s);
+  st = run_route(cfg, x, w_router, bias, gumbel_u, (routing && routing->logits) ? logits : nullptr, idx, tw, w, s);
   if (st != MOE_OK) return st;
   st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, x_perm, stats, w, s);
   if (st != MOE_OK) return st;

@@ -10,14 +10,29 @@
 // scores before the top-k.  Sigmoid scores normalised over the chosen experts
 // (bias for selection only) are the fine-grained workload's rule.
 //
-// One block = BT tokens x all experts.  Phase 1 computes z[BT][E] with f32 FMAs
-// from LDS tiles (K split across the four waves, blocked partial sums so the
-// error stays ~1e-7 of |z| at K = 12800).  Phase 2 gives each wave one token at
-// a time: lane l holds experts l, l+64, ... in registers, computes the keys in
-// float32 in a fixed operation order, and runs k rounds of a wave arg-max with
-// ties to the lower expert index.  Gate weights are formed in float64 and
-// rounded once.
+// bf16 activations (the MFMA path):
+//   router_prep   W_r [d,E] f32 -> Wt [3][EP][d] bf16 with W = hi + mid + lo
+//                 exactly (each part the bf16 rounding of what the previous
+//                 parts leave), transposed so K is contiguous for the MFMA
+//   router_mfma   z partials over d-slices: x (bf16, exact) times hi, mid and
+//                 lo on v_mfma_f32_16x16x32_bf16, accumulated in f32 -- every
+//                 product is exact, so z matches an f32 router to ~1e-7 at a
+//                 third of the bf16 MFMA rate; 8 waves x 32 tokens per block,
+//                 W tiles shared through LDS, d split across blocks so all CUs
+//                 work, partials written in [split][T][EP]
+//   topk          one wave per token: z = partials summed in split order, then
+//                 the keys / top-k / weights below
+// f32 activations (tiny workloads): one fused SIMT kernel -- phase 1 computes
+// z[BT][E] with f32 FMAs from LDS tiles (K split across the four waves,
+// blocked partial sums), phase 2 is the same per-token routine.
+//
+// Per-token routine: lane l holds experts l, l+64, ... in registers, computes
+// the keys in float32 in a fixed operation order, and runs k rounds of a wave
+// arg-max with ties to the lower expert index.  Gate weights are formed in
+// float64 and rounded once.
 #include <float.h>
+
+#include <algorithm>
 
 #include "common.h"
 
@@ -57,6 +72,116 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m));
   return v;
+}
+
+// Keys, wavefront top-k and gate weights of token t, executed by one whole wave.
+// zget(e) returns the token's f32 logit of expert e (e < E).  Lane l holds
+// experts l, l + 64, ... in registers; k rounds of a wave arg-max pick the
+// largest keys, ties to the lower index; weights are formed in float64.
+template <int EPL, typename ZGet>
+__device__ __forceinline__ void route_token(const RouteLaunch& a, int t, int lane, ZGet zget) {
+  const int E = a.E;
+  const float tau = a.tau;
+  float key[EPL], basis[EPL];
+  bool taken[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    const int e = lane + 64 * i;
+    taken[i] = !(e < E);
+    key[i] = 0.f;
+    basis[i] = 0.f;
+    if (e < E) {
+      const float z = zget(e);
+      if (a.logits) a.logits[(size_t)t * E + e] = z;
+      if (a.score == MOE_SCORE_SOFTMAX) {
+        float l = z;
+        if (a.bias_mode == MOE_BIAS_LOGIT) l = l + a.bias[e];
+        if (a.gumbel_u) {
+          const double u = (double)a.gumbel_u[(size_t)t * E + e];
+          l = l + (float)(-log(-log(u)));
+        }
+        l = l / tau;
+        basis[i] = l;
+        key[i] = (a.bias_mode == MOE_BIAS_SELECT_ONLY) ? l + a.bias[e] : l;
+      } else {
+        const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
+        basis[i] = s;
+        key[i] = (a.bias_mode == MOE_BIAS_SELECT_ONLY) ? s + a.bias[e] : s;
+      }
+    }
+  }
+
+  // k rounds of arg-max; slot j of the result is owned by lane j % 64, register j / 64
+  int sel_e[4];
+  float sel_b[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) { sel_e[s] = 0; sel_b[s] = 0.f; }
+  for (int j = 0; j < a.k; ++j) {
+    Cand c{-FLT_MAX, 0.f, INT32_MAX};
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      Cand o{key[i], basis[i], taken[i] ? INT32_MAX : lane + 64 * i};
+      if (better(o, c)) c = o;
+    }
+    c = wave_argmax(c);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+      if (c.e == lane + 64 * i) taken[i] = true;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if ((j >> 6) == s && (j & 63) == lane) { sel_e[s] = c.e; sel_b[s] = c.basis; }
+  }
+
+  // gate weights in float64
+  double w[4] = {0.0, 0.0, 0.0, 0.0};
+  if (a.score == MOE_SCORE_SOFTMAX) {
+    if (a.renormalize) {
+      float m = -FLT_MAX;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (lane + 64 * s < a.k) m = fmaxf(m, sel_b[s]);
+      m = wave_max(m);
+      double part = 0.0;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (lane + 64 * s < a.k) { w[s] = exp((double)sel_b[s] - (double)m); part += w[s]; }
+      const double sum = wave_sum(part);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) w[s] /= sum;
+    } else {
+      float M = -FLT_MAX;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i < E) M = fmaxf(M, basis[i]);
+      M = wave_max(M);
+      double part = 0.0;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (lane + 64 * i < E) part += exp((double)basis[i] - (double)M);
+      const double sum = wave_sum(part);
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        if (lane + 64 * s < a.k) w[s] = exp((double)sel_b[s] - (double)M) / sum;
+    }
+  } else {
+    double part = 0.0;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      if (lane + 64 * s < a.k) { w[s] = (double)sel_b[s]; part += w[s]; }
+    if (a.renormalize) {
+      const double sum = wave_sum(part);
+#pragma unroll
+      for (int s = 0; s < 4; ++s) w[s] /= sum;
+    }
+  }
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const int j = lane + 64 * s;
+    if (j < a.k) {
+      a.topk_idx[(size_t)t * a.k + j] = sel_e[s];
+      a.topk_w[(size_t)t * a.k + j] = (float)w[s];
+    }
+  }
 }
 
 template <bool BF16X, int EMAX, int BT, int ESPLIT, int TM, int TN>
@@ -168,111 +293,175 @@ __global__ __launch_bounds__(256) void route_kernel(RouteLaunch a) {
   }
 
   // ---- keys, wavefront top-k, gate weights: one token per wave at a time
-  const float tau = a.tau;
   for (int tl = wave; tl < BT; tl += 4) {
     const int t = t0 + tl;
     if (t >= T) break;  // uniform across the wave; no barrier below
-    float key[EPL], basis[EPL];
-    bool taken[EPL];
-#pragma unroll
-    for (int i = 0; i < EPL; ++i) {
-      const int e = lane + 64 * i;
-      taken[i] = !(e < E);
-      key[i] = 0.f;
-      basis[i] = 0.f;
-      if (e < E) {
-        const float z = zs[0][tl][e];
-        if (a.logits) a.logits[(size_t)t * E + e] = z;
-        if (a.score == MOE_SCORE_SOFTMAX) {
-          float l = z;
-          if (a.bias_mode == MOE_BIAS_LOGIT) l = l + a.bias[e];
-          if (a.gumbel_u) {
-            const double u = (double)a.gumbel_u[(size_t)t * E + e];
-            l = l + (float)(-log(-log(u)));
-          }
-          l = l / tau;
-          basis[i] = l;
-          key[i] = (a.bias_mode == MOE_BIAS_SELECT_ONLY) ? l + a.bias[e] : l;
-        } else {
-          const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
-          basis[i] = s;
-          key[i] = (a.bias_mode == MOE_BIAS_SELECT_ONLY) ? s + a.bias[e] : s;
-        }
-      }
-    }
-
-    // k rounds of arg-max; slot j of the result is owned by lane j % 64, register j / 64
-    int sel_e[4];
-    float sel_b[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) { sel_e[s] = 0; sel_b[s] = 0.f; }
-    for (int j = 0; j < a.k; ++j) {
-      Cand c{-FLT_MAX, 0.f, INT32_MAX};
-#pragma unroll
-      for (int i = 0; i < EPL; ++i) {
-        Cand o{key[i], basis[i], taken[i] ? INT32_MAX : lane + 64 * i};
-        if (better(o, c)) c = o;
-      }
-      c = wave_argmax(c);
-#pragma unroll
-      for (int i = 0; i < EPL; ++i)
-        if (c.e == lane + 64 * i) taken[i] = true;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if ((j >> 6) == s && (j & 63) == lane) { sel_e[s] = c.e; sel_b[s] = c.basis; }
-    }
-
-    // gate weights in float64
-    double w[4] = {0.0, 0.0, 0.0, 0.0};
-    if (a.score == MOE_SCORE_SOFTMAX) {
-      if (a.renormalize) {
-        float m = -FLT_MAX;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (lane + 64 * s < a.k) m = fmaxf(m, sel_b[s]);
-        m = wave_max(m);
-        double part = 0.0;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (lane + 64 * s < a.k) { w[s] = exp((double)sel_b[s] - (double)m); part += w[s]; }
-        const double sum = wave_sum(part);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) w[s] /= sum;
-      } else {
-        float M = -FLT_MAX;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          if (lane + 64 * i < E) M = fmaxf(M, basis[i]);
-        M = wave_max(M);
-        double part = 0.0;
-#pragma unroll
-        for (int i = 0; i < EPL; ++i)
-          if (lane + 64 * i < E) part += exp((double)basis[i] - (double)M);
-        const double sum = wave_sum(part);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-          if (lane + 64 * s < a.k) w[s] = exp((double)sel_b[s] - (double)M) / sum;
-      }
-    } else {
-      double part = 0.0;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        if (lane + 64 * s < a.k) { w[s] = (double)sel_b[s]; part += w[s]; }
-      if (a.renormalize) {
-        const double sum = wave_sum(part);
-#pragma unroll
-        for (int s = 0; s < 4; ++s) w[s] /= sum;
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int j = lane + 64 * s;
-      if (j < a.k) {
-        a.topk_idx[(size_t)t * a.k + j] = sel_e[s];
-        a.topk_w[(size_t)t * a.k + j] = (float)w[s];
-      }
-    }
+    route_token<EPL>(a, t, lane, [&](int e) { return zs[0][tl][e]; });
   }
+}
+
+// ---------------------------------------------------------------- MFMA path
+#define MOE_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
+#define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ void bar() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// W_r [d][E] f32 -> Wt [3][EP][d] bf16 (rows e >= E are zero).  Block: 64 k x 64 e.
+__global__ __launch_bounds__(256) void router_prep_kernel(const float* __restrict__ w, uint16_t* __restrict__ wt,
+                                                          int d, int E, int EP) {
+  __shared__ float tile[64][65];
+  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+    const int r = i / 64, c = i % 64;
+    tile[r][c] = (e0 + c < E) ? w[(size_t)(k0 + r) * E + e0 + c] : 0.f;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
+    const int el = i / 8, kc = i % 8;  // expert, 8-wide k chunk
+    const int e = e0 + el;
+    if (e >= EP) continue;
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t h2 = 0, m2 = 0, l2 = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float v = tile[kc * 8 + q * 2 + h][el];
+        const uint16_t bh = f32_to_bf16_rne(v);
+        const float r1 = v - bf16_bits_to_f32(bh);
+        const uint16_t bm = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_bits_to_f32(bm);
+        const uint16_t bl = f32_to_bf16_rne(r2);
+        h2 |= (uint32_t)bh << (16 * h);
+        m2 |= (uint32_t)bm << (16 * h);
+        l2 |= (uint32_t)bl << (16 * h);
+      }
+      hi[q] = h2; mid[q] = m2; lo[q] = l2;
+    }
+    const size_t o = (size_t)e * d + k0 + kc * 8;
+    *(uint4*)(wt + o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+    *(uint4*)(wt + (size_t)EP * d + o) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+    *(uint4*)(wt + (size_t)2 * EP * d + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  }
+}
+
+struct RouterParams {
+  const uint16_t* x;   // [T, d]
+  const uint16_t* wt;  // [3][EP][d]
+  float* part;         // [split][T][EP]
+  int T, d, kslice;
+};
+
+// z partial of 256 tokens x EP experts over one d-slice (blockIdx.y).  8 waves,
+// wave w owns tokens 32 w .. 32 w + 31 and every expert.
+template <int EP>
+__global__ __launch_bounds__(512, 1) void router_mfma_kernel(RouterParams p) {
+  constexpr int NF = EP / 16;
+  constexpr int ROWS = 3 * EP;          // B rows: split-major (hi, mid, lo)
+  constexpr int STAGE = ROWS * 64;      // 32 k (64 bytes) per row
+  constexpr int NINS = ROWS / 16;       // 16-row load instructions per stage
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = p.T, d = p.d;
+  const int t0 = blockIdx.x * 256;
+  const int kb = blockIdx.y * p.kslice, ksteps = p.kslice / 32;
+  const int kg = lane >> 4;
+  // A fragments straight from global memory (rows past T repeat the last row)
+  const uint16_t* xa0 = p.x + (size_t)min(t0 + w * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const uint16_t* xa1 = p.x + (size_t)min(t0 + w * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
+  // B tile loads: 16 rows x 64 bytes per instruction, 16-byte chunk c of row r at slot c ^ ((r >> 1) & 3)
+  const int dr = lane >> 2;
+  const int dc = (lane & 3) ^ ((dr >> 1) & 3);
+  const uint16_t* wsrc = p.wt + (size_t)dr * d + kb + dc * 8;
+  const uint32_t bfrag = (uint32_t)((lane & 15) * 64 + ((kg ^ (((lane & 15) >> 1) & 3)) * 16));
+  auto issue = [&](int ks) {
+    uint8_t* st = smem + (ks & 1) * STAGE;
+    for (int q = w; q < NINS; q += 8)
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(wsrc + (size_t)q * 16 * d + ks * 32), MOE_LPTR(st + q * 1024),
+                                       16, 0, 0);
+  };
+  f32x4_t acc[2][NF];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < NF; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue(0);
+  bf16x8_t a0 = *(const bf16x8_t*)xa0, a1 = *(const bf16x8_t*)xa1;
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  bar();
+  for (int ks = 0; ks < ksteps; ++ks) {
+    bf16x8_t n0 = a0, n1 = a1;
+    if (ks + 1 < ksteps) {
+      issue(ks + 1);
+      n0 = *(const bf16x8_t*)(xa0 + (ks + 1) * 32);
+      n1 = *(const bf16x8_t*)(xa1 + (ks + 1) * 32);
+    }
+    const uint8_t* st = smem + (ks & 1) * STAGE;
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+      const bf16x8_t bh = *(const bf16x8_t*)(st + bfrag + (n * 16) * 64);
+      const bf16x8_t bm = *(const bf16x8_t*)(st + bfrag + (EP + n * 16) * 64);
+      const bf16x8_t bl = *(const bf16x8_t*)(st + bfrag + (2 * EP + n * 16) * 64);
+      acc[0][n] = mfma16x16x32(a0, bh, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bh, acc[1][n]);
+      acc[0][n] = mfma16x16x32(a0, bm, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bm, acc[1][n]);
+      acc[0][n] = mfma16x16x32(a0, bl, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bl, acc[1][n]);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step ks + 1 (B tile and A fragments) landed
+    bar();                                 // and every wave is done with this step's stage
+    a0 = n0;
+    a1 = n1;
+  }
+  float* out = p.part + (size_t)blockIdx.y * T * EP;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + w * 32 + m * 16 + (lane >> 4) * 4 + r;
+      if (t < T) {
+#pragma unroll
+        for (int n = 0; n < NF; ++n) out[(size_t)t * EP + n * 16 + (lane & 15)] = acc[m][n][r];
+      }
+    }
+}
+
+// one wave per token: z = sum of the d-slice partials in order, then route_token
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_kernel(RouteLaunch a) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= a.T) return;
+  const float* part = a.part;
+  const int S = a.split, EP = a.ep, T = a.T;
+  route_token<EPL>(a, t, lane, [&](int e) {
+    float z = 0.f;
+    for (int sp = 0; sp < S; ++sp) z += part[((size_t)sp * T + t) * EP + e];
+    return z;
+  });
+}
+
+template <int EP>
+moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
+  int tok = begin_launch("router_prep", s);
+  hipLaunchKernelGGL(router_prep_kernel, dim3(a.d / 64, (unsigned)ceil_div(EP, 64)), dim3(256), 0, s,
+                     a.w_router, a.wt, a.d, a.E, EP);
+  moe_status st = end_launch(tok, s);
+  if (st != MOE_OK) return st;
+  RouterParams rp{(const uint16_t*)a.x, a.wt, a.part, a.T, a.d, a.d / a.split};
+  tok = begin_launch("router_mfma", s);
+  hipLaunchKernelGGL(router_mfma_kernel<EP>, dim3((unsigned)ceil_div(a.T, 256), a.split), dim3(512), 0, s, rp);
+  st = end_launch(tok, s);
+  if (st != MOE_OK) return st;
+  tok = begin_launch("route_topk", s);
+  hipLaunchKernelGGL(topk_kernel<(EP + 63) / 64>, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+  return end_launch(tok, s);
 }
 
 template <bool BF16X, int EMAX, int BT, int ESPLIT, int TM, int TN>
@@ -297,7 +486,28 @@ moe_status dispatch(const RouteLaunch& a, hipStream_t s) {
 
 moe_status launch_route(const RouteLaunch& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
-  return a.act_dtype == MOE_BF16 ? dispatch<true>(a, s) : dispatch<false>(a, s);
+  if (a.act_dtype != MOE_BF16) return dispatch<false>(a, s);
+  switch (a.ep) {
+    case 16: return launch_mfma_route<16>(a, s);
+    case 32: return launch_mfma_route<32>(a, s);
+    case 64: return launch_mfma_route<64>(a, s);
+    case 128: return launch_mfma_route<128>(a, s);
+    default: return launch_mfma_route<256>(a, s);
+  }
+}
+
+void route_plan(int T, int d, int E, int act_dtype, int* ep, int* split) {
+  if (act_dtype != MOE_BF16) { *ep = 0; *split = 0; return; }
+  int p = 16;
+  while (p < E) p *= 2;
+  *ep = p;
+  // about one block per CU: token blocks x d-slices, the slice a multiple of 32
+  const int tblocks = (int)ceil_div(std::max(T, 1), 256);
+  const int target = std::max(1, device_cu_count() / tblocks);
+  const int steps = d / 32;
+  int sp = std::min(target, steps);
+  while (steps % sp) --sp;
+  *split = sp;
 }
 
 }  // namespace moe

@@ -97,7 +97,7 @@ def run_stages(inp: W.MoEInputs, out_dtype=W.DT_F32):
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
     idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    lib.moe_route(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, logits, idx, w)
+    lib.moe_route(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, logits, idx, w, ws)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
     offsets = torch.empty(E + 1, dtype=torch.int32, device=dev)
     dest = torch.empty((T, k), dtype=torch.int32, device=dev)

@@ -80,17 +80,22 @@ def test_entry_points_validate_before_launch(L):
     lib = L.lib()
     cfg = _cfg(L)
     dummy = ctypes.c_void_p(256)  # never dereferenced: every call below fails validation first
+    big = ctypes.c_size_t(1 << 40)
     # missing required pointers
-    assert lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None, None) == 1
+    assert lib.moe_route(ctypes.byref(cfg), None, None, None, None, None, None, None, dummy, big, None) == 1
     # a bias is required exactly when bias_mode != NONE
-    assert lib.moe_route(ctypes.byref(cfg), dummy, dummy, dummy, None, None, dummy, dummy, None) == 1
+    assert lib.moe_route(ctypes.byref(cfg), dummy, dummy, dummy, None, None, dummy, dummy, dummy, big, None) == 1
     cfgb = _cfg(L, bias_mode=W.BIAS_LOGIT)
-    assert lib.moe_route(ctypes.byref(cfgb), dummy, dummy, None, None, None, dummy, dummy, None) == 1
+    assert lib.moe_route(ctypes.byref(cfgb), dummy, dummy, None, None, None, dummy, dummy, dummy, big, None) == 1
     # Gumbel noise with sigmoid scoring is unsupported
     cfgs = _cfg(L, score=W.SCORE_SIGMOID)
-    assert lib.moe_route(ctypes.byref(cfgs), dummy, dummy, None, dummy, None, dummy, dummy, None) == 2
+    assert lib.moe_route(ctypes.byref(cfgs), dummy, dummy, None, dummy, None, dummy, dummy, dummy, big, None) == 2
     # misaligned x
-    assert lib.moe_route(ctypes.byref(cfg), ctypes.c_void_p(258), dummy, None, None, None, dummy, dummy, None) == 1
+    assert lib.moe_route(ctypes.byref(cfg), ctypes.c_void_p(258), dummy, None, None, None, dummy, dummy, dummy, big,
+                         None) == 1
+    # the bf16 router needs its workspace
+    assert lib.moe_route(ctypes.byref(cfg), dummy, dummy, None, None, None, dummy, dummy, dummy, 64, None) == 3
+    assert lib.moe_route(ctypes.byref(cfg), dummy, dummy, None, None, None, dummy, dummy, None, 0, None) == 1
     # workspace too small / missing / misaligned
     args = [dummy] * 8
     assert lib.moe_permute(ctypes.byref(cfg), *args, dummy, 16, None) == 3
