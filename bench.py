@@ -53,9 +53,15 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
     hb = 4 if sh.w_dtype == W.DT_F32 else 2
     T, d, E, k, F, N = sh.T, sh.d, sh.E, sh.k, sh.F, kept_rows
     scale_b = 4 * (2 * F + d) if sh.w_dtype == W.DT_FP8 else 0
+    ep = 16
+    while ep < E:
+        ep *= 2
     work = {
-        # router: x once, W_r once, logits/indices/weights out
-        "route_topk": {"flop": 2.0 * T * d * E, "bytes": T * d * a + d * E * 4 + T * k * 8},
+        # router GEMM: x once, the split router weights once (algorithmic FLOP: the f32 product)
+        "router_mfma": {"flop": 2.0 * T * d * E, "bytes": T * d * a + 3 * ep * d * 2},
+        "router_prep": {"bytes": d * E * 4 + 3 * ep * d * 2},
+        # top-k: logits in, indices and weights out (the d-slice partials are extra traffic)
+        "route_topk": {"bytes": T * E * 4 + T * k * 8},
         "permute_hist": {"bytes": T * k * 4},
         "permute_scan": {"bytes": 0},
         "permute_rank": {"bytes": T * k * 8 + N * 4},

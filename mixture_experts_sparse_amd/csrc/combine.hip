@@ -35,6 +35,20 @@ __device__ __forceinline__ float4 load_parts(const float4* __restrict__ first, c
 }
 
 template <bool BF16OUT>
+__device__ __forceinline__ void store_out(void* out, size_t off, const float4& acc) {
+  if (BF16OUT) {
+    uint2 o;
+    o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
+    o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
+    ((uint2*)out)[off] = o;
+  } else {
+    ((float4*)out)[off] = acc;
+  }
+}
+
+// One wave per token; each lane handles U 16-byte vectors of the row per trip,
+// issuing every load of the trip before the first FMA (U k-slot rows in flight).
+template <bool BF16OUT, int U>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm,
                                                       const float4* __restrict__ y_shared,
                                                       const int32_t* __restrict__ dest_row,
@@ -46,29 +60,42 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
   if (t >= T) return;
   const int32_t* dr = dest_row + (size_t)t * k;
   const float* wt = topk_w + (size_t)t * k;
-  for (int v = lane; v < vec_per_row; v += 64) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int v0 = lane; v0 < vec_per_row; v0 += 64 * U) {
+    float4 acc[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
     for (int j = 0; j < k; ++j) {
       const int row = dr[j];
       if (row < 0 || row >= rows) continue;  // dropped (or out of range: ignored)
       const float w = wt[j];
-      const float4 y = load_parts(y_perm, yp, (size_t)row * vec_per_row + v);
-      acc.x = fmaf(w, y.x, acc.x);
-      acc.y = fmaf(w, y.y, acc.y);
-      acc.z = fmaf(w, y.z, acc.z);
-      acc.w = fmaf(w, y.w, acc.w);
+      float4 y[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + 64 * u;
+        y[u] = (v < vec_per_row) ? load_parts(y_perm, yp, (size_t)row * vec_per_row + v) : make_float4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        acc[u].x = fmaf(w, y[u].x, acc[u].x);
+        acc[u].y = fmaf(w, y[u].y, acc[u].y);
+        acc[u].z = fmaf(w, y[u].z, acc[u].z);
+        acc[u].w = fmaf(w, y[u].w, acc[u].w);
+      }
     }
     if (y_shared) {
-      const float4 s = load_parts(y_shared, sp, (size_t)t * vec_per_row + v);
-      acc.x += s.x; acc.y += s.y; acc.z += s.z; acc.w += s.w;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + 64 * u;
+        if (v < vec_per_row) {
+          const float4 s = load_parts(y_shared, sp, (size_t)t * vec_per_row + v);
+          acc[u].x += s.x; acc[u].y += s.y; acc[u].z += s.z; acc[u].w += s.w;
+        }
+      }
     }
-    if (BF16OUT) {
-      uint2 o;
-      o.x = (uint32_t)f32_to_bf16_rne(acc.x) | ((uint32_t)f32_to_bf16_rne(acc.y) << 16);
-      o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
-      ((uint2*)out)[(size_t)t * vec_per_row + v] = o;
-    } else {
-      ((float4*)out)[(size_t)t * vec_per_row + v] = acc;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + 64 * u;
+      if (v < vec_per_row) store_out<BF16OUT>(out, (size_t)t * vec_per_row + v, acc[u]);
     }
   }
 }
@@ -83,10 +110,10 @@ moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows) {
   const Parts sp{(const float4*)a.sh_rest, a.sh_stride / 4, a.sh_split};
   int tok = begin_launch("combine", s);
   if (a.out_dtype == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, s, (const float4*)a.y_perm,
+    hipLaunchKernelGGL((combine_kernel<true, 4>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
                        (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, s, (const float4*)a.y_perm,
+    hipLaunchKernelGGL((combine_kernel<false, 4>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
                        (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
   return end_launch(tok, s);
 }

@@ -327,9 +327,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // tiles evenly (wave tile 128 x 128, or 128 x 64 for narrower outputs), else the
 // 128 x 128 kernel (fp8, and bf16 shapes the large tiles do not divide), else
 // the fp32 SIMT kernel.
-// whether the large-tile bf16 kernel (256 x 256 block tiles) runs this pass
+// Kernel choice per pass (rows per group estimated as max_rows / groups):
+//   stream (bm 64 or 32): fp8 weights, or bf16 groups of fewer than 128 rows --
+//          bound by reading the weights, so small tiles and full-line streams;
+//   big (bm 256): bf16 groups of hundreds of rows -- bound by the matrix cores;
+//   128 x 128 kernel: any shape the two do not divide; SIMT kernel for fp32.
+static bool stream_shape_ok(const GemmLaunch& a) {
+  return a.K % 128 == 0 && (a.gated ? (a.N % 128 == 0) : (a.N % 256 == 0));
+}
+static int stream_bm(const GemmLaunch& a) {
+  if (a.w_dtype == MOE_F32 || !stream_shape_ok(a)) return 0;
+  const int64_t per_group = ceil_div(a.max_rows, std::max(a.groups, 1));
+  if (a.w_dtype == MOE_BF16 && per_group >= 128) return 0;
+  return per_group <= 32 ? 32 : 64;
+}
 static bool use_big(const GemmLaunch& a) {
-  if (a.w_dtype != MOE_BF16 || a.K % 64) return false;
+  if (a.w_dtype != MOE_BF16 || a.K % 64 || stream_bm(a)) return false;
   return a.gated ? (a.N % 128 == 0) : (a.N % 256 == 0);
 }
 
@@ -339,6 +352,8 @@ int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype) {
   probe.K = K;
   probe.N = N;
   probe.gated = false;
+  probe.max_rows = rows;
+  probe.groups = groups;
   if (!use_big(probe) || rows <= 0) return 1;
   // expected work units: m-tiles (with about half a ragged tile per busy group) x n-tiles x split
   const int64_t mt = ceil_div(rows, 256);
@@ -387,7 +402,8 @@ moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int s
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   const bool f32 = (a.w_dtype == MOE_F32);
   const bool big = use_big(a);
-  const int bm = f32 ? SM : (big ? 256 : MB);
+  const int sbm = stream_bm(a);
+  const int bm = f32 ? SM : (big ? 256 : (sbm ? sbm : MB));
   int32_t* goff = a.tile_prefix;
   int32_t* tp = a.tile_prefix + (a.groups + 1);
   int tok = begin_launch("gemm_tiles", s);
@@ -397,6 +413,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   if (st != MOE_OK) return st;
 
   if (big) return launch_gemm_bf16_big(a, goff, tp, s);
+  if (sbm) return launch_gemm_stream(a, goff, tp, sbm, s);
   GemmParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
   const int64_t mt_upper = ceil_div(a.max_rows, bm) + a.groups;
   if (f32) {

@@ -35,4 +35,8 @@ __device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int 
 // bf16 large-tile grouped GEMM (gemm_big.hip): block tile 256 x 256, 8 waves of 128 x 64
 moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s);
 
+// weight-streaming grouped GEMM for groups of few rows (gemm_stream.hip): bf16 or
+// fp8 weights, bm = 32 or 64 rows per tile, 256 weight rows per block
+moe_status launch_gemm_stream(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int bm, hipStream_t s);
+
 }  // namespace moe

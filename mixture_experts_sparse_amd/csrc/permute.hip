@@ -141,22 +141,33 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
     if (r >= n_rows) src_token[r] = -1;
 }
 
-// One wave per token: the row is read once (16-byte vectors) and written to
-// every kept destination.
+// One wave per token: the row is read once (16-byte vectors, four per lane in
+// flight) and written to every kept destination.
 __global__ __launch_bounds__(kThreads) void scatter_kernel(const uint4* __restrict__ x,
                                                            const int32_t* __restrict__ dest_row,
                                                            uint4* __restrict__ x_perm, int T,
                                                            int vec_per_row, int k) {
+  constexpr int U = 4;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const uint4* src = x + (size_t)t * vec_per_row;
   const int32_t* dr = dest_row + (size_t)t * k;
-  for (int v = lane; v < vec_per_row; v += 64) {
-    const uint4 val = src[v];
+  for (int v0 = lane; v0 < vec_per_row; v0 += 64 * U) {
+    uint4 val[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int v = v0 + 64 * u;
+      val[u] = (v < vec_per_row) ? src[v] : make_uint4(0, 0, 0, 0);
+    }
     for (int j = 0; j < k; ++j) {
       const int row = dr[j];
-      if (row >= 0) x_perm[(size_t)row * vec_per_row + v] = val;
+      if (row < 0) continue;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int v = v0 + 64 * u;
+        if (v < vec_per_row) x_perm[(size_t)row * vec_per_row + v] = val[u];
+      }
     }
   }
 }

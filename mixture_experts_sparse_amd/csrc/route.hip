@@ -415,7 +415,8 @@ __global__ __launch_bounds__(512, 1) void router_mfma_kernel(RouterParams p) {
       acc[1][n] = mfma16x16x32(a1, bl, acc[1][n]);
     }
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): step ks + 1 (B tile and A fragments) landed
-    bar();                                 // and every wave is done with this step's stage
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's reads of this step's stage are done
+    bar();                                 // so after the barrier the stage may be refilled
     a0 = n0;
     a1 = n1;
   }
@@ -441,8 +442,19 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteLaunch a) {
   const float* part = a.part;
   const int S = a.split, EP = a.ep, T = a.T;
   route_token<EPL>(a, t, lane, [&](int e) {
+    // partials added in split order; loads issued eight at a time
+    const float* pe = part + (size_t)t * EP + e;
+    const size_t st = (size_t)T * EP;
     float z = 0.f;
-    for (int sp = 0; sp < S; ++sp) z += part[((size_t)sp * T + t) * EP + e];
+    int sp = 0;
+    for (; sp + 8 <= S; sp += 8) {
+      float v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] = pe[(size_t)(sp + q) * st];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) z += v[q];
+    }
+    for (; sp < S; ++sp) z += pe[(size_t)sp * st];
     return z;
   });
 }

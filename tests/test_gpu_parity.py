@@ -18,7 +18,9 @@ SMALL = {
     "mixtral_small": W.shrink(WK["mixtral_bf16"], T=1000, d=512, F=1024),
     "gumbel_small": W.shrink(WK["gumbel_bf16"], T=300, d=384, F=256),
     "fine_shared_small": W.shrink(WK["fine_shared_bf16"], T=150, d=256, F=128),
-    "skewed_fp8_small": W.shrink(WK["skewed_fp8"], T=700, d=256, F=192),
+    "skewed_fp8_small": W.shrink(WK["skewed_fp8"], T=700, d=256, F=256),
+    "fp8_odd_F": W.shrink(WK["skewed_fp8"], T=300, d=256, F=192),
+    "bf16_stream": WK["mixtral_bf16"].replace(name="bf16s", T=333, d=512, E=32, k=4, F=384),
     "skewed_fp8_decode": WK["skewed_fp8_decode"],
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
