@@ -42,7 +42,44 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 512 MiB device copy first (HBM counter calibration)")
+    ap.add_argument("--weight-copies", type=int, default=0,
+                    help="expert-weight copies the steps rotate through (0: 3 when T <= 1024, else 1), "
+                         "so a small step's weights are not served from the 256 MB MALL")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """sha256 over every kernel source; a traffic record taken with other sources
+    no longer describes the kernels that run."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_sparse_amd", "csrc")
+    files = sorted(f for f in os.listdir(csrc) if f.endswith((".hip", ".h")))
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 FETCH_SIZE / WRITE_SIZE record
+    (profiles/*.md, a line `traffic_record: {json}`), if it was taken on these sources."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    want = kernel_source_hash()
+    for f in sorted(os.listdir(pdir)):
+        if not f.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, f)) as fh:
+            for line in fh:
+                if not line.startswith("traffic_record: "):
+                    continue
+                rec = json.loads(line[len("traffic_record: "):])
+                if rec.get("kernel") == kernel and rec.get("workload") == workload \
+                        and rec.get("source_sha256") == want:
+                    return rec
+    return None
 
 
 def algorithmic_work(sh, kept_rows: int, touched: int):
@@ -141,32 +178,40 @@ def main():
         del src, dst
     inp = W.make_inputs(sh, device=dev)
     cfg = L.make_config(sh)
-    weights = L.expert_weights(inp)
+    copies = args.weight_copies or (3 if sh.T <= 1024 else 1)
+    weight_sets = [L.expert_weights(inp)]
+    keep = []
+    for _ in range(copies - 1):
+        c = inp.clone_weights()
+        keep.append(c)
+        weight_sets.append(L.expert_weights(c))
     ws = L.alloc_workspace(cfg, dev)
     out = torch.empty((sh.T, sh.d), dtype=torch.float32, device=dev)
     stats = torch.empty(2 * sh.E + 1, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     print("[bench] inputs ready", file=sys.stderr, flush=True)
 
-    def step():
-        L.moe_forward(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, weights, out, stats, ws)
+    def step(i):
+        L.moe_forward(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, weight_sets[i % copies], out,
+                      stats, ws)
 
-    for _ in range(args.warmup):
-        step()
+    for i in range(args.warmup):
+        step(i)
     torch.cuda.synchronize()
     L.moe_profile_read()  # discard anything recorded before
     L.moe_profile_enable(True)
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        step()
-    stop.record()
+    marks[0].record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+        marks[i + 1].record()
     torch.cuda.synchronize()
     L.moe_profile_enable(False)
     prof = L.moe_profile_read()
-    ms_total = start.elapsed_time(stop)
+    ms_total = marks[0].elapsed_time(marks[-1])
     ms_step = ms_total / args.steps
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     st = stats.cpu().numpy()
     kept = int(st[sh.E:2 * sh.E].sum())
     touched = int((st[sh.E:2 * sh.E] > 0).sum())
@@ -193,12 +238,17 @@ def main():
     # dominant kernel: the largest share of the step time
     dom = max(prof.items(), key=lambda kv: kv[1][1])[0]
     dk = kernels[dom]
+    rec = recorded_traffic(dom, sh.name)
+    traffic = None if rec is None else rec["bytes_per_launch"]
     if "tflops" in dk and ("gate_up" in dom or "down" in dom):
         roof = {"kernel": dom, "bound": "mfma", "achieved": dk["tflops"], "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": dk["mfma_frac"], "traffic": None}
+                "unit": "TFLOP/s", "frac": dk["mfma_frac"], "traffic": traffic}
     else:
         roof = {"kernel": dom, "bound": "hbm", "achieved": dk.get("gbs"), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": dk.get("hbm_frac"), "traffic": None}
+                "unit": "GB/s", "frac": dk.get("hbm_frac"), "traffic": traffic}
+    if rec is not None:
+        roof["traffic_unit"] = "bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"
+        roof["traffic_algorithmic"] = work.get(kernel_key(dom), {}).get("bytes")
 
     res = {
         "metric": METRIC,
@@ -208,6 +258,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "step_ms": {"p10": round(float(np.percentile(per_step, 10)), 4),
+                    "median": round(float(np.median(per_step)), 4),
+                    "p90": round(float(np.percentile(per_step, 90)), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -216,7 +269,8 @@ def main():
         "config": {"workload": sh.name, "T": sh.T, "d": sh.d, "E": sh.E, "top_k": sh.k, "F": sh.F,
                    "n_shared": sh.n_shared, "weights": dt_name, "router": "f32",
                    "capacity_factor": sh.capacity_factor or None, "kept_rows": kept,
-                   "touched_experts": touched, "dropped": int(st[2 * sh.E])},
+                   "touched_experts": touched, "dropped": int(st[2 * sh.E]),
+                   "weight_copies": copies},
         "roofline": roof,
         "kernels": kernels,
     }

@@ -229,6 +229,15 @@ class MoEInputs:
             kw[f.name] = v.to(device) if isinstance(v, torch.Tensor) else v
         return MoEInputs(**kw)
 
+    def clone_weights(self) -> "MoEInputs":
+        """Same values, expert weights (and scales) in freshly allocated memory."""
+        kw = {}
+        for f in dataclasses.fields(self):
+            v = getattr(self, f.name)
+            copy = f.name.startswith(("w_gate", "w_up", "w_down", "s_", "sh_"))
+            kw[f.name] = v.clone() if copy and isinstance(v, torch.Tensor) else v
+        return MoEInputs(**kw)
+
 
 def make_inputs(shape: MoEShape, device="cpu", seed: Optional[int] = None) -> MoEInputs:
     """Draw every input of one MoE-layer call for ``shape`` on ``device``."""
