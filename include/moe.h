@@ -50,8 +50,8 @@
  *    W_gate, W_up are [E, F, d], W_down is [E, d, F].  fp8 weights are OCP
  *    e4m3fn codes with one float32 scale per output row ([E,F], [E,F], [E,d]).
  *  - Limits: 1 <= top_k <= E <= 256; T >= 0 (T = 0 is a no-op);
- *    d % 128 == 0 and F % 64 == 0 for bf16/fp8 weights, d % 64 == 0 and
- *    F % 64 == 0 for fp32 weights; T * top_k < 2^31.
+ *    d % 128 == 0 always; F % 64 == 0 for bf16/fp8 weights, F % 32 == 0
+ *    for fp32 weights; T * top_k < 2^31.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
