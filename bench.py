@@ -211,7 +211,7 @@ def main():
     prof = L.moe_profile_read()
     ms_total = marks[0].elapsed_time(marks[-1])
     ms_step = ms_total / args.steps
-    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    step_times = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
     st = stats.cpu().numpy()
     kept = int(st[sh.E:2 * sh.E].sum())
     touched = int((st[sh.E:2 * sh.E] > 0).sum())
@@ -258,9 +258,9 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
-        "step_ms": {"p10": round(float(np.percentile(per_step, 10)), 4),
-                    "median": round(float(np.median(per_step)), 4),
-                    "p90": round(float(np.percentile(per_step, 90)), 4)},
+        "step_ms": {"p10": round(float(np.percentile(step_times, 10)), 4),
+                    "median": round(float(np.median(step_times)), 4),
+                    "p90": round(float(np.percentile(step_times, 90)), 4)},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

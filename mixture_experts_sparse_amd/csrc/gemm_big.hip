@@ -5,21 +5,22 @@
 // page "GPT-4 has 1.8T parameters but uses 2% per token" (mlqm.cn), s3.3
 // SwiGLU), organised for gfx950's matrix cores:
 //
-//  * block tile 256 rows x (2 WN) weight rows; four waves (2 x 2), each owning a
-//    128 x WN output tile with its accumulators in AGPRs (128 x 128: 256 AGPRs);
-//    LDS bytes read per MFMA are half those of 64 x 64 wave tiles;
-//  * K step 64 per LDS stage (128-byte rows: every fetch is a whole cache
-//    line), two stages of 64 KB, filled by direct global -> LDS loads
-//    (global_load_lds_dwordx4: lane i of a load lands at base + 16 i), so the
-//    prefetch costs no VGPRs;
+//  * block tile 256 rows x 256 weight rows; eight waves as 2 (M) x 4 (N), each
+//    owning a 128 x 64 output tile (128 f32 accumulators per lane);
+//  * K step 64 (128-byte LDS rows: every fetch is a whole cache line), filled
+//    by direct global -> LDS loads (global_load_lds_dwordx4: lane i of a load
+//    lands at base + 16 i), so the prefetch costs no VGPRs.  The activation
+//    tile has two 32 KB stages, the weight tile three: the weights are the
+//    HBM-first traffic, so their loads get two K steps to land, the activation
+//    rows (shared by eight CUs of an XCD and cache-resident) one.  160 KB in all;
 //  * 16-byte chunk c of row r is stored at slot c ^ (r & 7): the 16x16x32
 //    fragment reads (row = lane % 16, chunk = lane / 16 (+4)) are then free of
 //    bank conflicts.  The swizzle is applied on the load side by choosing
 //    which global chunk each lane fetches;
 //  * each K step is two 32-wide halves with their own fragment registers: the
 //    fragments of one half are read while the MFMAs of the other issue; the
-//    single s_barrier of a step sits between the halves, after which the
-//    step-after-next is requested into the stage just consumed;
+//    single s_barrier of a step sits between the halves, after which the next
+//    loads are requested into the stages just consumed;
 //  * the eight load instructions and the fragment reads of a half are spread
 //    one per MFMA row (scheduling barriers keep that order), so the memory
 //    pipeline never receives a burst that would stall MFMA issue.
@@ -70,12 +71,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
   constexpr int BNR = WAVES_N * WN;          // 256 weight rows per block
   constexpr int A_BYTES = kBM * kRow;        // 32 KB
   constexpr int B_BYTES = BNR * kRow;        // 32 KB
-  constexpr int STAGE = A_BYTES + B_BYTES;   // 64 KB; two stages
+  constexpr int A_STAGES = 2, B_STAGES = 3;
+  constexpr int B_BASE = A_STAGES * A_BYTES; // weight stages follow the activation stages
   constexpr int NJ = WN / 16;                // B fragments per wave
   constexpr int A_INS = A_BYTES / 1024 / NW; // 4 DMA instructions (8 rows each) per wave
   constexpr int B_INS = B_BYTES / 1024 / NW; // 4
   static_assert(A_INS + B_INS == 8, "one load per MFMA row");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[A_STAGES * A_BYTES + B_STAGES * B_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
@@ -95,8 +97,8 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
   const int kg = lane >> 4;                       // k group of the fragment (8 values each)
   const uint32_t a_frag0 = (uint32_t)((wm * 128 + frow) * kRow + ((kg ^ (frow & 7)) * 16));
   const uint32_t a_frag1 = (uint32_t)((wm * 128 + frow) * kRow + (((kg + 4) ^ (frow & 7)) * 16));
-  const uint32_t b_frag0 = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + ((kg ^ (frow & 7)) * 16));
-  const uint32_t b_frag1 = (uint32_t)(A_BYTES + (wn * WN + frow) * kRow + (((kg + 4) ^ (frow & 7)) * 16));
+  const uint32_t b_frag0 = (uint32_t)((wn * WN + frow) * kRow + ((kg ^ (frow & 7)) * 16));
+  const uint32_t b_frag1 = (uint32_t)((wn * WN + frow) * kRow + (((kg + 4) ^ (frow & 7)) * 16));
 
   for (int U = xcd * chunk + jb; U < lend; U += G8) {
     const int part = U / tiles, L = U - part * tiles;
@@ -130,17 +132,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
       }
       b_base[i] = (const uint8_t*)base + ((size_t)g * N * K + (size_t)wrow0 * K) * 2 + kofs;
     }
-    // load instruction q (0..7) of step ks; steps past the last are clamped to
-    // it (they refill the stage just consumed, which no later step reads)
+    // load instruction q (0..7) of step ks into that step's stage (activation
+    // stage ks % 2, weight stage ks % 3); steps past the last are clamped to it
+    // (they refill a stage just consumed, which no later step reads)
     auto load_one = [&](int q, int ks) {
-      uint8_t* st = smem + (ks & 1) * STAGE;
       const uint32_t kb = (uint32_t)min(ks, ksteps - 1) * kRow;
       if (q < A_INS)
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[q] + kb), MOE_LPTR(st + (w * A_INS + q) * 1024),
-                                         16, 0, 0);
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[q] + kb),
+                                         MOE_LPTR(smem + (ks & 1) * A_BYTES + (w * A_INS + q) * 1024), 16, 0, 0);
       else
         __builtin_amdgcn_global_load_lds(MOE_GPTR(b_base[q - A_INS] + b_off + kb),
-                                         MOE_LPTR(st + A_BYTES + (w * B_INS + q - A_INS) * 1024), 16, 0, 0);
+                                         MOE_LPTR(smem + B_BASE + (ks % 3) * B_BYTES + (w * B_INS + q - A_INS) * 1024),
+                                         16, 0, 0);
     };
 
     f32x4_t acc[8][NJ];
@@ -151,43 +154,54 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     bf16x8_t X[8 + NJ], Y[8 + NJ];  // fragments of the first / second 32-wide half of a step
 
     block_sync();  // every wave is done with the previous unit's stages
+    // activations of steps 0 and 1, weights of steps 0, 1 and 2 (in this order:
+    // loads complete in issue order, so a count of outstanding loads names them)
 #pragma unroll
     for (int q = 0; q < 8; ++q) load_one(q, 0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) load_one(q, 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));  // step 0 has landed
+#pragma unroll
+    for (int q = A_INS; q < 8; ++q) load_one(q, 2);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + B_INS));  // step 0 has landed
     block_sync();
 #pragma unroll
     for (int i = 0; i < 8; ++i) X[i] = *(const bf16x8_t*)(smem + a_frag0 + i * 2048);
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) X[8 + j] = *(const bf16x8_t*)(smem + b_frag0 + j * 2048);
+    for (int j = 0; j < NJ; ++j) X[8 + j] = *(const bf16x8_t*)(smem + B_BASE + b_frag0 + j * 2048);
 
+    int bs = 0;  // weight stage of step ks (ks % 3)
     for (int ks = 0; ks < ksteps; ++ks) {
-      const uint8_t* sc = smem + (ks & 1) * STAGE;
-      const uint8_t* sn = smem + ((ks + 1) & 1) * STAGE;
+      const int bn = bs == 2 ? 0 : bs + 1;
+      const uint8_t* sa = smem + (ks & 1) * A_BYTES;
+      const uint8_t* sb = smem + B_BASE + bs * B_BYTES;
+      const uint8_t* na = smem + ((ks + 1) & 1) * A_BYTES;
+      const uint8_t* nb = smem + B_BASE + bn * B_BYTES;
       // first half: MFMAs on X, second-half fragments of this step read alongside
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        Y[i] = *(const bf16x8_t*)(sc + a_frag1 + i * 2048);
-        if (i < NJ) Y[8 + i] = *(const bf16x8_t*)(sc + b_frag1 + i * 2048);
+        Y[i] = *(const bf16x8_t*)(sa + a_frag1 + i * 2048);
+        if (i < NJ) Y[8 + i] = *(const bf16x8_t*)(sb + b_frag1 + i * 2048);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[i], X[8 + j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // step ks + 1 has landed
-      __builtin_amdgcn_s_waitcnt(kLgkm0);         // this wave's reads of step ks are done
+      // step ks + 1 has landed; only the weights of step ks + 2 may still be in flight
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(B_INS));
+      __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's reads of step ks are done
       block_sync();
-      // second half: MFMAs on Y; step ks + 2 requested into this step's stage and
-      // the first-half fragments of step ks + 1 read, one of each per MFMA row
+      // second half: MFMAs on Y; the activations of step ks + 2 and the weights of
+      // step ks + 3 requested into the stages step ks has released, and the
+      // first-half fragments of step ks + 1 read, one of each per MFMA row
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        load_one(i, ks + 2);
-        X[i] = *(const bf16x8_t*)(sn + a_frag0 + i * 2048);
-        if (i < NJ) X[8 + i] = *(const bf16x8_t*)(sn + b_frag0 + i * 2048);
+        load_one(i, i < A_INS ? ks + 2 : ks + 3);
+        X[i] = *(const bf16x8_t*)(na + a_frag0 + i * 2048);
+        if (i < NJ) X[8 + i] = *(const bf16x8_t*)(nb + b_frag0 + i * 2048);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[i], Y[8 + j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      bs = bn;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this unit
 
