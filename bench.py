@@ -12,7 +12,7 @@ input already resident in HBM.  Prints one JSON line:
               algorithmic FLOP or bytes per launch, rate, fraction of peak)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
 
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload mixtral_bf16]
+Usage: python bench.py [--gpus 1] [--steps 50] [--warmup 20] [--workload mixtral_bf16]
 """
 from __future__ import annotations
 
@@ -35,8 +35,9 @@ DEFAULT_WORKLOAD = "mixtral_bf16"
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=50)
+    # the GPU clocks take a few tens of milliseconds of load to settle
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")

@@ -164,6 +164,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     for (int q = A_INS; q < 8; ++q) load_one(q, 2);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + B_INS));  // step 0 has landed
     block_sync();
+
+    if (wm * 128 >= tr.rows) {
+      // every row of this wave is padding (a tile of at most 128 rows): it
+      // skips the fragment reads and MFMAs and only takes its share of the
+      // loads, with the same waits and the same one barrier per step
+      for (int ks = 0; ks < ksteps; ++ks) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B_INS));
+        block_sync();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_one(i, i < A_INS ? ks + 2 : ks + 3);
+      }
+    } else {
 #pragma unroll
     for (int i = 0; i < 8; ++i) X[i] = *(const bf16x8_t*)(smem + a_frag0 + i * 2048);
 #pragma unroll
@@ -202,6 +214,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       bs = bn;
+    }
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this unit
 
@@ -265,8 +278,7 @@ moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const 
               a.split_rest, a.split_stride};
   p.n_tiles = a.gated ? a.N / 128 : a.N / 256;
   const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles * p.split;
-  int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count());
-  grid = ceil_div(grid, 8) * 8;
+  int64_t grid = ceil_div(upper, 8) * 8;
   if (grid <= 0) return MOE_OK;
   const char* name = a.shared ? (a.gated ? "shared_gate_up_bf16" : "shared_down_bf16")
                               : (a.gated ? "gemm_gate_up_bf16" : "gemm_down_bf16");

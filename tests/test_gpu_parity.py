@@ -21,6 +21,11 @@ SMALL = {
     "skewed_fp8_small": W.shrink(WK["skewed_fp8"], T=700, d=256, F=256),
     "fp8_odd_F": W.shrink(WK["skewed_fp8"], T=300, d=256, F=192),
     "bf16_stream": WK["mixtral_bf16"].replace(name="bf16s", T=333, d=512, E=32, k=4, F=384),
+    # large-tile path with ragged groups: Zipf-biased rows per expert
+    # [800, 13, 0, 5, 130, 0, 652, 0] give tiles of 32, 13 and 5 rows (whose
+    # second 128-row half is all padding), a 130-row tile and empty experts
+    "bf16_skewed_big": WK["mixtral_bf16"].replace(name="bf16z", T=800, d=256, E=8, k=2, F=256,
+                                                  bias_mode=W.BIAS_LOGIT, bias_kind="zipf1.2"),
     "skewed_fp8_decode": WK["skewed_fp8_decode"],
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
