@@ -21,9 +21,11 @@
 //    fragments of one half are read while the MFMAs of the other issue; the
 //    single s_barrier of a step sits between the halves, after which the next
 //    loads are requested into the stages just consumed;
-//  * the eight load instructions and the fragment reads of a half are spread
-//    one per MFMA row (scheduling barriers keep that order), so the memory
-//    pipeline never receives a burst that would stall MFMA issue.
+//  * the eight load instructions of a step are spread one per MFMA row and the
+//    twelve fragment reads of a half two per row over the first six rows
+//    (scheduling barriers keep that order), so the memory pipeline never gets
+//    a burst and the reads have landed before the barrier or the next step
+//    waits for them.
 #include <algorithm>
 
 #include "grouped.h"
@@ -176,10 +178,18 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
         for (int i = 0; i < 8; ++i) load_one(i, i < A_INS ? ks + 2 : ks + 3);
       }
     } else {
+    // fragment entry e of a half: weights first (every MFMA row needs all of
+    // them), then the activation rows
+    auto read_frag = [&](bf16x8_t (&F)[8 + NJ], int e, const uint8_t* sa, const uint8_t* sb, uint32_t af,
+                         uint32_t bf) {
+      if (e < NJ) F[8 + e] = *(const bf16x8_t*)(sb + bf + e * 2048);
+      else F[e - NJ] = *(const bf16x8_t*)(sa + af + (e - NJ) * 2048);
+    };
 #pragma unroll
-    for (int i = 0; i < 8; ++i) X[i] = *(const bf16x8_t*)(smem + a_frag0 + i * 2048);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) X[8 + j] = *(const bf16x8_t*)(smem + B_BASE + b_frag0 + j * 2048);
+    for (int e = 0; e < 8 + NJ; ++e) read_frag(X, e, smem, smem + B_BASE, a_frag0, b_frag0);
+    // nothing may be pending at the loop head (tile lookups leave scalar loads in
+    // flight, which would make the compiler drain the counter there every step)
+    __builtin_amdgcn_s_waitcnt(kLgkm0);
 
     int bs = 0;  // weight stage of step ks (ks % 3)
     for (int ks = 0; ks < ksteps; ++ks) {
@@ -191,8 +201,10 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
       // first half: MFMAs on X, second-half fragments of this step read alongside
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        Y[i] = *(const bf16x8_t*)(sa + a_frag1 + i * 2048);
-        if (i < NJ) Y[8 + i] = *(const bf16x8_t*)(sb + b_frag1 + i * 2048);
+        // the 12 fragment reads of the half go out over the first six MFMA rows,
+        // so they have landed before anything waits for them
+#pragma unroll
+        for (int e = 2 * i; e < 2 * i + 2 && e < 8 + NJ; ++e) read_frag(Y, e, sa, sb, a_frag1, b_frag1);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[i], X[8 + j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
@@ -207,12 +219,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         load_one(i, i < A_INS ? ks + 2 : ks + 3);
-        X[i] = *(const bf16x8_t*)(na + a_frag0 + i * 2048);
-        if (i < NJ) X[8 + i] = *(const bf16x8_t*)(nb + b_frag0 + i * 2048);
+#pragma unroll
+        for (int e = 2 * i; e < 2 * i + 2 && e < 8 + NJ; ++e) read_frag(X, e, na, nb, a_frag0, b_frag0);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[i], Y[8 + j], acc[i][j]);
         __builtin_amdgcn_sched_barrier(0);
       }
+      __builtin_amdgcn_s_waitcnt(kLgkm0);  // next step's first-half fragments are in
       bs = bn;
     }
     }
