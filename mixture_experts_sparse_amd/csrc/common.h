@@ -93,7 +93,7 @@ constexpr int kPermChunk = 1024;
 struct PermuteLaunch {
   const void* x; const int32_t* topk_idx;
   int32_t* counts; int32_t* offsets; int32_t* dest_row; int32_t* src_token; int32_t* n_dropped;
-  void* x_perm;
+  void* x_perm;          // null: the rows are not copied (the GEMM gathers them from x)
   int32_t* stats;        // [2E+1] or null
   int32_t* hist;         // workspace [nblocks * E]
   int T, d, E, k, act_bytes;
@@ -136,11 +136,16 @@ struct GemmLaunch {
   int w_dtype;              // MOE_F32 / MOE_BF16 / MOE_FP8_E4M3FN
   bool gated;
   bool shared;              // the shared expert (names its launches apart)
+  const int32_t* gather = nullptr;  // row r of A is A[gather[r]] (A = x, gather = src_token), or
+                                    // null for a dense A; only kernels that gather_ok() admits
   int split_k = 1;          // down pass: K split into parts; part 0 goes to `out`,
   float* split_rest = nullptr;  // part p >= 1 to split_rest + (p - 1) * split_stride
   size_t split_stride = 0;  // elements
 };
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+// whether the kernel launch_grouped_gemm picks for `a` can read A through a.gather
+// (row byte offsets into A must also fit 32 bits: A_rows * K * 2 < 2^32)
+bool gather_ok(const GemmLaunch& a, int64_t a_rows);
 
 // K-split chosen for a down pass of `rows` rows (1 = no split); the large-tile
 // kernel is the only one that splits.  Deterministic function of the shape.

@@ -399,10 +399,16 @@ moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int s
   return end_launch(tok, s);
 }
 
+bool gather_ok(const GemmLaunch& a, int64_t a_rows) {
+  if (!use_big(a) && !stream_bm(a)) return false;
+  return a_rows * (int64_t)a.K * 2 < ((int64_t)1 << 32);
+}
+
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   const bool f32 = (a.w_dtype == MOE_F32);
   const bool big = use_big(a);
   const int sbm = stream_bm(a);
+  if (a.gather && !big && !sbm) return fail(MOE_ERR_UNSUPPORTED, "row gather needs the large-tile or streaming GEMM");
   const int bm = f32 ? SM : (big ? 256 : (sbm ? sbm : MB));
   int32_t* goff = a.tile_prefix;
   int32_t* tp = a.tile_prefix + (a.groups + 1);

@@ -64,6 +64,7 @@ struct BigParams {
   int split;             // K split into this many parts (down pass only)
   float* split_rest;     // part p >= 1 goes to split_rest + (p - 1) * split_stride
   size_t split_stride;
+  const int32_t* gather; // A row r is A[gather[r]], or null
 };
 
 // Waves: 2 along M (128 rows each) x 4 along N (64 weight rows each).
@@ -109,12 +110,15 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     const size_t kofs = (size_t)part * kpart * 2;  // byte offset of this K part
 
     // load sources: wave-uniform bases plus 32-bit per-lane byte offsets
-    const uint8_t* a_base = (const uint8_t*)p.A + (size_t)tr.row0 * K * 2 + kofs;
+    // rows past the group's end repeat its last row; with a gather map the rows
+    // come straight from the token matrix (offsets checked to fit 32 bits)
+    const uint8_t* a_base = (const uint8_t*)p.A + (p.gather ? 0 : (size_t)tr.row0 * K * 2) + kofs;
     uint32_t a_off[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
-      const int r = (w * A_INS + i) * 8 + dma_row;
-      a_off[i] = (uint32_t)((min(r, tr.rows - 1) * K + dma_chunk * 8) * 2);
+      const int r = min((w * A_INS + i) * 8 + dma_row, tr.rows - 1);
+      const uint32_t src = p.gather ? (uint32_t)p.gather[tr.row0 + r] : (uint32_t)r;
+      a_off[i] = (src * (uint32_t)K + (uint32_t)(dma_chunk * 8)) * 2u;
     }
     const uint32_t b_off = (uint32_t)((dma_row * K + dma_chunk * 8) * 2);
     const uint8_t* b_base[B_INS];
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
 // goff / tile prefix already built for 256-row tiles.
 moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s) {
   BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gated ? 1 : a.split_k,
-              a.split_rest, a.split_stride};
+              a.split_rest, a.split_stride, a.gather};
   p.n_tiles = a.gated ? a.N / 128 : a.N / 256;
   const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles * p.split;
   int64_t grid = ceil_div(upper, 8) * 8;

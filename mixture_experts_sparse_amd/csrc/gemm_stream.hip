@@ -58,6 +58,7 @@ struct StreamParams {
   const int32_t* goff;
   const int32_t* tp;
   int groups, K, N, n_tiles;
+  const int32_t* gather;  // A row r is A[gather[r]], or null
 };
 
 // 8 bf16 for sub-step s from a lane's raw weight registers
@@ -108,13 +109,17 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
   for (int L = xcd * chunk + jb; L < lend; L += G8) {
     const TileRef tr = map_tile(L, p.n_tiles, p.groups, BM, p.tp, p.goff);
     const int g = tr.g;
-    const uint8_t* a_base = (const uint8_t*)p.A + (size_t)tr.row0 * K * 2;
+    // rows past the group's end repeat its last row; with a gather map the rows
+    // come straight from the token matrix (offsets checked to fit 32 bits)
+    const uint8_t* a_base = (const uint8_t*)p.A + (p.gather ? 0 : (size_t)tr.row0 * K * 2);
     uint32_t a_off[A_INS];
 #pragma unroll
     for (int i = 0; i < A_INS; ++i) {
       const int r = (w * A_INS + i) * 4 + dma_r;
       const int c = (lane & 15) ^ (r & 15);
-      a_off[i] = (uint32_t)((size_t)min(r, tr.rows - 1) * K * 2 + c * 16);
+      const int rr = min(r, tr.rows - 1);
+      const uint32_t src = p.gather ? (uint32_t)p.gather[tr.row0 + rr] : (uint32_t)rr;
+      a_off[i] = src * (uint32_t)K * 2u + (uint32_t)(c * 16);
     }
     // this lane's weight rows (one per n-fragment), k offset 32 g4
     const uint8_t* b_row[NF];
@@ -272,7 +277,7 @@ moe_status launch_t(const StreamParams& p, int mf, int64_t grid, hipStream_t s) 
 }  // namespace
 
 moe_status launch_gemm_stream(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int bm, hipStream_t s) {
-  StreamParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
+  StreamParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gather};
   p.n_tiles = a.gated ? a.N / 128 : a.N / 256;
   const int64_t upper = (ceil_div(a.max_rows, bm) + a.groups) * p.n_tiles;
   int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count() * 2);

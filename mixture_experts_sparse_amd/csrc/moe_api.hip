@@ -265,23 +265,33 @@ moe_status run_permute(const moe_config* c, const void* x, const int32_t* topk_i
   return launch_permute(p, s);
 }
 
+// The routed gate/up pass: A = x_perm, or A = x read through `gather` (src_token).
+GemmLaunch gate_up_launch(const moe_config* c, const void* x, const void* x_perm, const int32_t* gather,
+                          const int32_t* offsets, const moe_expert_weights* w, char* ws) {
+  const Layout L = layout_of(c);
+  GemmLaunch g{};
+  g.w_dtype = c->w_dtype;
+  g.A = gather ? x : x_perm; g.gather = gather;
+  g.B0 = w->w_gate; g.B1 = w->w_up; g.S0 = w->s_gate; g.S1 = w->s_up;
+  g.out = ws + L.h; g.offsets = offsets; g.tile_prefix = (int32_t*)(ws + L.tiles);
+  g.groups = c->E; g.single_rows = 0; g.max_rows = perm_rows(c); g.K = c->d; g.N = c->F; g.gated = true;
+  return g;
+}
+
 // reduce_partials: fold the down pass's K-split partial sums into y_perm / y_shared
 // (the standalone entry point); moe_forward leaves them for the combine to add.
-moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const int32_t* offsets,
-                   const moe_expert_weights* w, float* y_perm, float* y_shared, char* ws, bool reduce_partials,
-                   hipStream_t s) {
+// gather: src_token when the gate/up pass reads x directly (x_perm is then unused).
+moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const int32_t* gather,
+                   const int32_t* offsets, const moe_expert_weights* w, float* y_perm, float* y_shared, char* ws,
+                   bool reduce_partials, hipStream_t s) {
   if (c->T == 0) return MOE_OK;
   const Layout L = layout_of(c);
   const int64_t R = perm_rows(c);
-  GemmLaunch g{};
-  g.w_dtype = c->w_dtype;
   // routed experts: gate/up pass then down pass
-  g.A = x_perm; g.B0 = w->w_gate; g.B1 = w->w_up; g.S0 = w->s_gate; g.S1 = w->s_up;
-  g.out = ws + L.h; g.offsets = offsets; g.tile_prefix = (int32_t*)(ws + L.tiles);
-  g.groups = c->E; g.single_rows = 0; g.max_rows = R; g.K = c->d; g.N = c->F; g.gated = true;
+  GemmLaunch g = gate_up_launch(c, x, x_perm, gather, offsets, w, ws);
   moe_status st = launch_grouped_gemm(g, s);
   if (st != MOE_OK) return st;
-  g.A = ws + L.h; g.B0 = w->w_down; g.B1 = nullptr; g.S0 = w->s_down; g.S1 = nullptr;
+  g.A = ws + L.h; g.gather = nullptr; g.B0 = w->w_down; g.B1 = nullptr; g.S0 = w->s_down; g.S1 = nullptr;
   g.out = y_perm; g.K = c->F; g.N = c->d; g.gated = false;
   g.split_k = L.split; g.split_rest = (float*)(ws + L.y_rest); g.split_stride = (size_t)R * c->d;
   st = launch_grouped_gemm(g, s);
@@ -411,7 +421,8 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_pe
   }
   st = check_ws(ws, ws_bytes, layout_of(cfg).ffn_end);
   if (st != MOE_OK) return st;
-  return run_ffn(cfg, x, x_perm, offsets, weights, y_perm, y_shared, (char*)ws, true, (hipStream_t)stream);
+  return run_ffn(cfg, x, x_perm, nullptr, offsets, weights, y_perm, y_shared, (char*)ws, true,
+                 (hipStream_t)stream);
 }
 
 moe_status moe_combine(const moe_config* cfg, const float* y_perm, const float* y_shared, const int32_t* dest_row,
@@ -460,9 +471,12 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
 
   st = run_route(cfg, x, w_router, bias, gumbel_u, (routing && routing->logits) ? logits : nullptr, idx, tw, w, s);
   if (st != MOE_OK) return st;
-  st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, x_perm, stats, w, s);
+  // gather fusion: when the gate/up kernel can read the token rows through
+  // src_token, the permute writes no x_perm and the rows are read once, by the GEMM
+  const bool gather = cfg->T > 0 && gather_ok(gate_up_launch(cfg, x, x_perm, src, offsets, weights, w), cfg->T);
+  st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, gather ? nullptr : x_perm, stats, w, s);
   if (st != MOE_OK) return st;
-  st = run_ffn(cfg, x, x_perm, offsets, weights, y_perm, y_sh, w, false, s);
+  st = run_ffn(cfg, x, x_perm, gather ? src : nullptr, offsets, weights, y_perm, y_sh, w, false, s);
   if (st != MOE_OK) return st;
   return run_combine(cfg, y_perm, y_sh, dest, tw, out, w, s);
 }

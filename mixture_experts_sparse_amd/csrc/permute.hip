@@ -211,6 +211,7 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
   st = end_launch(tok, s);
   if (st != MOE_OK) return st;
 
+  if (!a.x_perm) return MOE_OK;
   const int vec_per_row = a.d * a.act_bytes / 16;
   tok = begin_launch("permute_scatter", s);
   hipLaunchKernelGGL(scatter_kernel, dim3((unsigned)ceil_div(a.T, 4)), dim3(kThreads), 0, s,

@@ -517,7 +517,9 @@ void route_plan(int T, int d, int E, int act_dtype, int* ep, int* split) {
   const int tblocks = (int)ceil_div(std::max(T, 1), 256);
   const int target = std::max(1, device_cu_count() / tblocks);
   const int steps = d / 32;
-  int sp = std::min(target, steps);
+  // at least eight 32-wide steps per slice: for few tokens the grid stays small
+  // and the top-k pass has few partials to add
+  int sp = std::min(target, std::max(1, steps / 8));
   while (steps % sp) --sp;
   *split = sp;
 }
