@@ -198,6 +198,54 @@ def route_from_logits(z, rc: RouteConfig, bias=None, u=None) -> Routing:
 
 
 # ---------------------------------------------------------------------------
+# load-balancing statistics and the loss-free bias update (after the layer)
+def router_probs(z, rc: RouteConfig, bias=None, u=None) -> np.ndarray:
+    """Each token's probability of each expert, float64 [T, E].
+
+    [P3] s4.3 (training stability, auxiliary loss) uses router_probs, every
+    token's probability for every expert, without saying how it is formed.
+    Reading: the distribution the gate weights are drawn from, before the top-k
+    -- for softmax scoring the softmax over all E experts of the weight basis l
+    (logit bias, Gumbel noise and temperature included, exactly as in the keys;
+    a selection-only bias is not part of l), for sigmoid scoring the sigmoid
+    scores normalised to sum 1 (the selection-only bias again left out).
+    """
+    _, basis = selection_keys(z, rc, bias, u)
+    b = np.asarray(basis, np.float64)
+    if rc.score == SCORE_SOFTMAX:
+        ex = np.exp(b - b.max(axis=1, keepdims=True))
+        return ex / ex.sum(axis=1, keepdims=True)
+    return b / b.sum(axis=1, keepdims=True)
+
+
+def router_stats(probs, counts):
+    """Mean router probability per expert, and the auxiliary-loss term.
+
+    [P3] s4.3: aux_loss = sum_e mean_t(router_probs[t, e]) * expert_count[e],
+    expert_count[e] = how often expert e was chosen over all top-k slots (the
+    requested counts, before any capacity limit).  The caller scales it (the
+    page adds 0.01 * aux_loss to the main loss).  Returns (prob_mean [E]
+    float64, aux float).
+    """
+    P = np.asarray(probs, np.float64).mean(axis=0)
+    return P, float(np.sum(P * np.asarray(counts, np.float64)))
+
+
+def bias_update(bias, counts, decay: float = 0.99, rate: float = 0.01) -> np.ndarray:
+    """One loss-free balancing step on the per-expert selection bias, float32 [E].
+
+    [P5] gating network code (balancing without an auxiliary loss): load[e] =
+    how often expert e was chosen over all top-k slots; ratio = load /
+    (mean(load) + 1e-8); bias <- decay * bias - rate * ratio, so busy experts'
+    biases fall below idle ones'.  Its routing configuration sets decay 0.99
+    and rate 0.01.  Computed in float64 and rounded once.
+    """
+    load = np.asarray(counts, np.float64)
+    ratio = load / (load.mean() + 1e-8)
+    return (float(decay) * np.asarray(bias, np.float64) - float(rate) * ratio).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------
 # S3 capacity, counts, stable ranks; S4 permutation
 def capacity(T: int, k: int, E: int, capacity_factor: float) -> Optional[int]:
     """C = max(1, floor(T * k / E * cf)); None (no limit) when cf <= 0.

@@ -15,7 +15,7 @@ import tests.test_oracle_pins as pins
 _orig = {name: getattr(O, name) for name in
          ["router_logits", "gumbel_noise", "topk_by_keys", "gate_weights", "capacity",
           "permute", "swiglu_ffn", "combine", "fp8_e4m3fn_decode", "selection_keys",
-          "silu"]}
+          "silu", "router_probs", "router_stats", "bias_update"]}
 
 
 def m_router_wrong_column(x, w):
@@ -78,6 +78,34 @@ def m_bias_in_weights(z, rc, bias=None, u=None):
     return key, basis
 
 
+def m_probs_with_selection_bias(z, rc, bias=None, u=None):
+    key, _ = O.selection_keys(z, rc, bias, u)
+    k = np.asarray(key, np.float64)
+    if rc.score == O.SCORE_SOFTMAX:
+        ex = np.exp(k - k.max(axis=1, keepdims=True))
+        return ex / ex.sum(axis=1, keepdims=True)
+    return k / k.sum(axis=1, keepdims=True)
+
+
+def m_probs_no_tau(z, rc, bias=None, u=None):
+    rc1 = O.RouteConfig(rc.E, rc.k, rc.score, rc.renormalize, 1.0, rc.bias_mode)
+    return _orig["router_probs"](z, rc1, bias, u)
+
+
+def m_stats_sum_not_mean(probs, counts):
+    P = np.asarray(probs, np.float64).sum(axis=0)
+    return P, float(np.sum(P * np.asarray(counts, np.float64)))
+
+
+def m_bias_wrong_sign(bias, counts, decay=0.99, rate=0.01):
+    load = np.asarray(counts, np.float64)
+    return (decay * np.asarray(bias, np.float64) + rate * load / (load.mean() + 1e-8)).astype(np.float32)
+
+
+def m_bias_unnormalised_load(bias, counts, decay=0.99, rate=0.01):
+    return (decay * np.asarray(bias, np.float64) - rate * np.asarray(counts, np.float64)).astype(np.float32)
+
+
 MUTATIONS = [
     ("router_logits", m_router_wrong_column, ["test_router_unit_vectors_select_rows"]),
     ("gumbel_noise", m_gumbel_sign, ["test_gumbel_statistics_match_gumbel01",
@@ -93,6 +121,12 @@ MUTATIONS = [
     ("combine", m_combine_unweighted, ["test_identity_expert_combine_inverts_permute"]),
     ("fp8_e4m3fn_decode", m_fp8_bias8, ["test_fp8_decode_all_codes"]),
     ("selection_keys", m_bias_in_weights, ["test_selection_only_bias_steers_but_does_not_weigh"]),
+    ("router_probs", m_probs_with_selection_bias,
+     ["test_router_probs_ignore_selection_only_bias_and_follow_logit_bias"]),
+    ("router_probs", m_probs_no_tau, ["test_router_probs_are_the_unrenormalised_gate_weights"]),
+    ("router_stats", m_stats_sum_not_mean, ["test_router_stats_hand_example_and_uniform_closed_form"]),
+    ("bias_update", m_bias_wrong_sign, ["test_bias_update_hand_examples"]),
+    ("bias_update", m_bias_unnormalised_load, ["test_bias_update_hand_examples"]),
 ]
 
 

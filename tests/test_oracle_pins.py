@@ -426,3 +426,82 @@ def test_token_outputs_agree_with_forward():
     toks = [0, 3, 29, 17]
     got = O.token_outputs(toks, x, res.perm.dest_row, res.routing.idx, res.routing.w, ew, sh)
     np.testing.assert_allclose(got, res.out[toks], rtol=1e-12, atol=1e-12)
+
+
+# ------------------------------------------------ load-balancing statistics
+def test_router_probs_uniform_logits_give_uniform():
+    """Equal logits give 1/E for every expert, in every scoring mode (closed form)."""
+    z = np.zeros((3, 6), np.float32)
+    for rc in (O.RouteConfig(6, 2), O.RouteConfig(6, 2, tau=0.5),
+               O.RouteConfig(6, 2, score=O.SCORE_SIGMOID, bias_mode=O.BIAS_SELECT_ONLY)):
+        b = np.linspace(-1, 1, 6).astype(np.float32) if rc.bias_mode else None
+        p = O.router_probs(z, rc, b)
+        np.testing.assert_allclose(p, 1.0 / 6, rtol=0, atol=1e-15)
+
+
+def test_router_probs_are_the_unrenormalised_gate_weights():
+    """The page's no-renormalisation weights are the top-k entries of the softmax
+    over all E, so router_probs at the chosen experts must equal them (Gumbel
+    noise and temperature included, as in the perturbed-softmax workload)."""
+    r = _rng(11)
+    z = r.standard_normal((20, 16)).astype(np.float32)
+    u = ((r.integers(0, 1 << 23, (20, 16)) + 0.5) * 2.0 ** -23).astype(np.float32)
+    rc = O.RouteConfig(16, 2, renormalize=0, tau=0.5)
+    p = O.router_probs(z, rc, None, u)
+    ro = O.route_from_logits(z, rc, None, u)
+    np.testing.assert_allclose(np.take_along_axis(p, ro.idx.astype(np.int64), 1), ro.w, rtol=2e-7)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=1e-14)
+
+
+def test_router_probs_ignore_selection_only_bias_and_follow_logit_bias():
+    """A selection-only bias steers the top-k but is not part of the probabilities;
+    a logit bias of +log(3) on one expert triples its odds against every other."""
+    r = _rng(12)
+    z = r.standard_normal((7, 5)).astype(np.float32)
+    b = r.standard_normal(5).astype(np.float32)
+    for score in (O.SCORE_SOFTMAX, O.SCORE_SIGMOID):
+        p0 = O.router_probs(z, O.RouteConfig(5, 2, score=score))
+        p1 = O.router_probs(z, O.RouteConfig(5, 2, score=score, bias_mode=O.BIAS_SELECT_ONLY), b)
+        np.testing.assert_array_equal(p0, p1)
+    bl = np.zeros(5, np.float32)
+    bl[2] = np.float32(math.log(3.0))
+    z0 = np.zeros((1, 5), np.float32)
+    p = O.router_probs(z0, O.RouteConfig(5, 1, bias_mode=O.BIAS_LOGIT), bl)[0]
+    np.testing.assert_allclose(p[2] / p[0], 3.0, rtol=1e-6)
+    np.testing.assert_allclose(p, [1 / 7, 1 / 7, 3 / 7, 1 / 7, 1 / 7], rtol=1e-6)
+
+
+def test_router_probs_sigmoid_scores_normalised():
+    """Sigmoid scoring: logits log(1), log(3) give sigmoid 1/2 and 3/4, so the
+    probabilities are 2/5 and 3/5 (hand-computed)."""
+    z = np.array([[0.0, math.log(3.0)]], np.float32)
+    p = O.router_probs(z, O.RouteConfig(2, 1, score=O.SCORE_SIGMOID))[0]
+    np.testing.assert_allclose(p, [0.4, 0.6], rtol=1e-7)
+
+
+def test_router_stats_hand_example_and_uniform_closed_form():
+    """aux = sum_e mean_t(p) * count: p rows (1, 0) and (1/2, 1/2) average to
+    (3/4, 1/4); with counts (3, 1) the sum is 3/4*3 + 1/4*1 = 5/2.  With uniform
+    probabilities the term is T k / E whatever the counts."""
+    P, aux = O.router_stats(np.array([[1.0, 0.0], [0.5, 0.5]]), np.array([3, 1]))
+    np.testing.assert_allclose(P, [0.75, 0.25])
+    assert aux == pytest.approx(2.5, rel=1e-15)
+    r = _rng(13)
+    T, E, k = 50, 8, 2
+    counts = np.bincount(r.integers(0, E, T * k), minlength=E)
+    _, aux_u = O.router_stats(np.full((T, E), 1.0 / E), counts)
+    assert aux_u == pytest.approx(T * k / E, rel=1e-13)
+
+
+def test_bias_update_hand_examples():
+    """counts (3, 1): mean 2, ratios (3/2, 1/2); bias (0.2, -0.1) becomes
+    (0.99*0.2 - 0.015, 0.99*(-0.1) - 0.005) = (0.183, -0.104).  Balanced counts
+    give ratio 1 (every bias decays and drops by the rate); no traffic leaves
+    only the decay."""
+    b = O.bias_update(np.array([0.2, -0.1], np.float32), np.array([3, 1]))
+    np.testing.assert_allclose(b, [0.183, -0.104], rtol=0, atol=1e-7)
+    b2 = O.bias_update(np.array([0.5, 0.0, -0.5], np.float32), np.array([4, 4, 4]), 0.9, 0.1)
+    np.testing.assert_allclose(b2, [0.35, -0.1, -0.55], rtol=0, atol=1e-7)
+    b3 = O.bias_update(np.array([1.0, -2.0], np.float32), np.array([0, 0]))
+    np.testing.assert_allclose(b3, [0.99, -1.98], rtol=0, atol=1e-7)
+    assert b.dtype == np.float32
