@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--cpu-sample", type=int, default=0, help="tokens in the oracle sample (0: auto)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a plain 512 MiB device copy first (HBM counter calibration)")
+    ap.add_argument("--balance", action="store_true",
+                    help="each step also runs the load-balancing statistics and the bias step "
+                         "(moe_router_stats, moe_bias_update on a scratch bias)")
     ap.add_argument("--weight-copies", type=int, default=0,
                     help="expert-weight copies the steps rotate through (0: 3 when T <= 1024, else 1), "
                          "so a small step's weights are not served from the 256 MB MALL")
@@ -115,6 +118,8 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
         "combine": {"bytes": N * d * 4 + T * d * (4 if sh.out_dtype == W.DT_F32 else 2)
                     + T * k * 8 + (T * d * 4 if sh.n_shared else 0)},
     }
+    # load balancing (--balance): the logits (and Gumbel uniforms) read once
+    work["balance_stats"] = {"bytes": T * E * 4 * (2 if sh.gumbel else 1)}
     if sh.n_shared:
         work["shared_gate_up"] = {"flop": 4.0 * T * d * F, "bytes": T * d * a + 2 * F * d * wb + T * F * hb}
         work["shared_down"] = {"flop": 2.0 * T * F * d, "bytes": T * F * hb + d * F * wb + T * d * 4}
@@ -192,9 +197,20 @@ def main():
     torch.cuda.synchronize()
     print("[bench] inputs ready", file=sys.stderr, flush=True)
 
+    routing = None
+    if args.balance:
+        routing = {"logits": torch.empty((sh.T, sh.E), dtype=torch.float32, device=dev)}
+        prob_mean = torch.empty(sh.E, dtype=torch.float32, device=dev)
+        aux = torch.empty(1, dtype=torch.float32, device=dev)
+        scratch_bias = torch.zeros(sh.E, dtype=torch.float32, device=dev)
+        counts = stats[: sh.E]
+
     def step(i):
         L.moe_forward(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, weight_sets[i % copies], out,
-                      stats, ws)
+                      stats, ws, routing=routing)
+        if args.balance:
+            L.moe_router_stats(cfg, routing["logits"], inp.bias, inp.gumbel_u, counts, prob_mean, aux, ws)
+            L.moe_bias_update(cfg, counts, scratch_bias)
 
     for i in range(args.warmup):
         step(i)
@@ -271,7 +287,7 @@ def main():
                    "n_shared": sh.n_shared, "weights": dt_name, "router": "f32",
                    "capacity_factor": sh.capacity_factor or None, "kept_rows": kept,
                    "touched_experts": touched, "dropped": int(st[2 * sh.E]),
-                   "weight_copies": copies},
+                   "weight_copies": copies, "balance": bool(args.balance)},
         "roofline": roof,
         "kernels": kernels,
     }

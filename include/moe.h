@@ -204,6 +204,35 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
                        const moe_routing_out* routing, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* ---- load balancing after a routed batch ----
+ * Mean router probability and the auxiliary-loss term ([P3] s4.3 training
+ * stability: aux = sum_e mean_t(router_probs[t,e]) * expert_count[e]).  The
+ * router probability of (t,e) is the distribution the gate weights are drawn
+ * from before the top-k: the softmax over all E experts of the weight basis
+ * (z, plus a logit bias, plus Gumbel noise, over tau) for softmax scoring, the
+ * sigmoid scores normalised to sum 1 for sigmoid scoring; a selection-only
+ * bias is not part of it.  Reduced in a fixed order in f64, rounded once.
+ *   logits    [T,E] f32: the router logits of the batch (moe_route's or
+ *             moe_forward's routing output)
+ *   bias      [E] f32 as given to the routing call (read for a logit bias)
+ *   gumbel_u  [T,E] f32 as given to the routing call, or NULL
+ *   counts    [E] int32: pairs routed to each expert, before any capacity
+ *             limit (moe_permute's counts; the first E entries of stats)
+ *   prob_mean [E] f32 out: mean over the T tokens (0 when T == 0)
+ *   aux       [1] f32 out, or NULL: sum_e prob_mean[e] * counts[e]
+ *   ws        device workspace of at least moe_workspace_bytes(cfg) bytes */
+moe_status moe_router_stats(const moe_config* cfg, const float* logits, const float* bias,
+                            const float* gumbel_u, const int32_t* counts, float* prob_mean,
+                            float* aux, void* ws, size_t ws_bytes, void* stream);
+
+/* One loss-free balancing step of the per-expert bias ([P5] gating network:
+ *   bias[e] <- decay * bias[e] - rate * counts[e] / (mean_e(counts) + 1e-8),
+ * decay 0.99 and rate 0.01 in its routing configuration), in f64, rounded once.
+ *   counts [E] int32 as for moe_router_stats;  bias [E] f32, updated in place.
+ *   decay, rate: finite. */
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float* bias,
+                           float decay, float rate, void* stream);
+
 /* ---- measurement hooks (not part of the layer) ----
  * While enabled on the calling thread, every kernel the library launches is
  * bracketed by HIP events recorded on the launch stream.  moe_profile_read()

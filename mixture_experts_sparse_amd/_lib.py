@@ -23,7 +23,8 @@ STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPOR
 # every symbol include/moe.h declares
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_bytes",
             "moe_permuted_rows", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-            "moe_forward", "moe_profile_enable", "moe_profile_read"]
+            "moe_forward", "moe_router_stats", "moe_bias_update", "moe_profile_enable",
+            "moe_profile_read"]
 
 
 class MoEError(RuntimeError):
@@ -75,6 +76,8 @@ def _load() -> ctypes.CDLL:
         "moe_combine": ([cfgp, P, P, P, P, P, P], ctypes.c_int),
         "moe_forward": ([cfgp, P, P, P, P, ctypes.POINTER(moe_expert_weights), P, P,
                          ctypes.POINTER(moe_routing_out), P, ctypes.c_size_t, P], ctypes.c_int),
+        "moe_router_stats": ([cfgp, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
+        "moe_bias_update": ([cfgp, P, P, ctypes.c_float, ctypes.c_float, P], ctypes.c_int),
         "moe_profile_enable": ([ctypes.c_int32], ctypes.c_int),
         "moe_profile_read": ([ctypes.POINTER(moe_kernel_time), ctypes.c_int32,
                               ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
@@ -182,6 +185,17 @@ def moe_forward(cfg, x, w_router, bias, gumbel_u, weights: moe_expert_weights, o
                             ctypes.byref(weights), _ptr(out), _ptr(stats),
                             ctypes.byref(r) if r is not None else None, _ptr(ws),
                             ws.numel() if ws is not None else 0, _stream(stream)), "moe_forward")
+
+
+def moe_router_stats(cfg, logits, bias, gumbel_u, counts, prob_mean, aux, ws, stream=None):
+    _check(_LIB.moe_router_stats(ctypes.byref(cfg), _ptr(logits), _ptr(bias), _ptr(gumbel_u), _ptr(counts),
+                                 _ptr(prob_mean), _ptr(aux), _ptr(ws), ws.numel() if ws is not None else 0,
+                                 _stream(stream)), "moe_router_stats")
+
+
+def moe_bias_update(cfg, counts, bias, decay: float = 0.99, rate: float = 0.01, stream=None):
+    _check(_LIB.moe_bias_update(ctypes.byref(cfg), _ptr(counts), _ptr(bias), ctypes.c_float(decay),
+                                ctypes.c_float(rate), _stream(stream)), "moe_bias_update")
 
 
 def moe_profile_enable(on: bool):

@@ -10,9 +10,12 @@
 //   out[t] = sum_{j: dest_row[t,j] >= 0} w[t,j] * y_perm[dest_row[t,j]]  (+ y_shared[t])
 //
 // Bandwidth-bound: one wave per token, 16-byte vector loads of the k source
-// rows (gathered by dest_row), f32 FMAs in j order, one store of the row.
+// rows (gathered by dest_row), four slots' rows in flight at once, f32 FMAs in
+// j order, one store of the row.
 // When the down projection split its reduction, the partial sums of a row are
 // added in part order first, so the result does not depend on scheduling.
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -46,9 +49,10 @@ __device__ __forceinline__ void store_out(void* out, size_t off, const float4& a
   }
 }
 
-// One wave per token; each lane handles U 16-byte vectors of the row per trip,
-// issuing every load of the trip before the first FMA (U k-slot rows in flight).
-template <bool BF16OUT, int U>
+// One wave per token; each lane handles U 16-byte vectors of the row per trip.
+// The rows of JB slots are requested together (JB x U loads in flight per lane)
+// and then added in slot order, so the sum is the same as one slot at a time.
+template <bool BF16OUT, int U, int JB>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm,
                                                       const float4* __restrict__ y_shared,
                                                       const int32_t* __restrict__ dest_row,
@@ -64,22 +68,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
     float4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const int row = dr[j];
-      if (row < 0 || row >= rows) continue;  // dropped (or out of range: ignored)
-      const float w = wt[j];
-      float4 y[U];
+    for (int j0 = 0; j0 < k; j0 += JB) {
+      int row[JB];
+      float w[JB];
+      float4 y[JB][U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int v = v0 + 64 * u;
-        y[u] = (v < vec_per_row) ? load_parts(y_perm, yp, (size_t)row * vec_per_row + v) : make_float4(0, 0, 0, 0);
+      for (int jj = 0; jj < JB; ++jj) {
+        const int j = j0 + jj;
+        row[jj] = j < k ? dr[j] : -1;
+        if (row[jj] >= rows) row[jj] = -1;  // out of range: ignored like a dropped slot
+        w[jj] = row[jj] >= 0 ? wt[j] : 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int v = v0 + 64 * u;
+          y[jj][u] = (row[jj] >= 0 && v < vec_per_row)
+                         ? load_parts(y_perm, yp, (size_t)row[jj] * vec_per_row + v) : make_float4(0, 0, 0, 0);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        acc[u].x = fmaf(w, y[u].x, acc[u].x);
-        acc[u].y = fmaf(w, y[u].y, acc[u].y);
-        acc[u].z = fmaf(w, y[u].z, acc[u].z);
-        acc[u].w = fmaf(w, y[u].w, acc[u].w);
+      for (int jj = 0; jj < JB; ++jj) {
+        if (row[jj] < 0) continue;  // dropped slots add nothing
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          acc[u].x = fmaf(w[jj], y[jj][u].x, acc[u].x);
+          acc[u].y = fmaf(w[jj], y[jj][u].y, acc[u].y);
+          acc[u].z = fmaf(w[jj], y[jj][u].z, acc[u].z);
+          acc[u].w = fmaf(w[jj], y[jj][u].w, acc[u].w);
+        }
       }
     }
     if (y_shared) {
@@ -109,12 +124,21 @@ moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows) {
   const Parts yp{(const float4*)a.y_rest, a.y_stride / 4, a.y_split};
   const Parts sp{(const float4*)a.sh_rest, a.sh_stride / 4, a.sh_split};
   int tok = begin_launch("combine", s);
-  if (a.out_dtype == MOE_BF16)
-    hipLaunchKernelGGL((combine_kernel<true, 4>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
+  // slots requested together: four at a time when a token has many (measured:
+  // one at a time is faster for k <= 2, where the extra registers cost occupancy)
+  auto go = [&](auto bf16_tag, auto jb_tag) {
+    constexpr bool B = decltype(bf16_tag)::value;
+    constexpr int JB = decltype(jb_tag)::value;
+    hipLaunchKernelGGL((combine_kernel<B, 4, JB>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
                        (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
-  else
-    hipLaunchKernelGGL((combine_kernel<false, 4>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
-                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
+  };
+  using I1 = std::integral_constant<int, 1>;
+  using I4 = std::integral_constant<int, 4>;
+  if (a.out_dtype == MOE_BF16) {
+    if (a.k <= 2) go(std::true_type{}, I1{}); else go(std::true_type{}, I4{});
+  } else {
+    if (a.k <= 2) go(std::false_type{}, I1{}); else go(std::false_type{}, I4{});
+  }
   return end_launch(tok, s);
 }
 

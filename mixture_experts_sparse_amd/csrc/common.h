@@ -102,6 +102,18 @@ struct PermuteLaunch {
 };
 moe_status launch_permute(const PermuteLaunch& a, hipStream_t s);
 
+// load-balancing statistics (balance.hip)
+struct RouterStatsLaunch {
+  const float* logits; const float* bias; const float* gumbel_u; const int32_t* counts;
+  float* prob_mean; float* aux;  // aux may be null
+  double* part;                  // workspace of router_stats_ws_bytes(T, E)
+  int T, E, score, bias_mode;
+  float tau;
+};
+int64_t router_stats_ws_bytes(int T, int E);
+moe_status launch_router_stats(const RouterStatsLaunch& a, hipStream_t s);
+moe_status launch_bias_update(const int32_t* counts, float* bias, int E, float decay, float rate, hipStream_t s);
+
 struct CombineLaunch {
   const float* y_perm; const float* y_shared; const int32_t* dest_row; const float* topk_w;
   void* out; int T, d, k, out_dtype;

@@ -196,7 +196,8 @@ Layout layout_of(const moe_config* c) {
   L.x_perm = take((size_t)dtype_bytes(c->act_dtype) * R * c->d);
   L.y_perm = take(sizeof(float) * R * c->d);
   L.y_sh = take(c->n_shared ? sizeof(float) * (size_t)c->T * c->d : 0);
-  L.total = o;
+  // moe_router_stats reuses the workspace for its per-block partial sums
+  L.total = std::max(o, (size_t)router_stats_ws_bytes(c->T, c->E));
   return L;
 }
 
@@ -354,7 +355,7 @@ const char* moe_status_string(moe_status s) {
 
 const char* moe_last_error(void) { return g_err; }
 
-int32_t moe_version(void) { return 100; }
+int32_t moe_version(void) { return 200; }
 
 moe_status moe_workspace_bytes(const moe_config* cfg, size_t* bytes) {
   g_err[0] = 0;
@@ -479,6 +480,36 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
   st = run_ffn(cfg, x, x_perm, gather ? src : nullptr, offsets, weights, y_perm, y_sh, w, false, s);
   if (st != MOE_OK) return st;
   return run_combine(cfg, y_perm, y_sh, dest, tw, out, w, s);
+}
+
+moe_status moe_router_stats(const moe_config* cfg, const float* logits, const float* bias,
+                            const float* gumbel_u, const int32_t* counts, float* prob_mean, float* aux,
+                            void* ws, size_t ws_bytes, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!counts || !prob_mean) return fail(MOE_ERR_INVALID_ARGUMENT, "counts and prob_mean must be non-NULL");
+  if (cfg->T > 0 && !logits) return fail(MOE_ERR_INVALID_ARGUMENT, "logits is NULL");
+  if (cfg->T > 0 && cfg->bias_mode == MOE_BIAS_LOGIT && !bias)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "a logit bias needs the bias vector");
+  if (gumbel_u && cfg->score != MOE_SCORE_SOFTMAX)
+    return fail(MOE_ERR_INVALID_ARGUMENT, "Gumbel noise needs softmax scoring");
+  st = check_ws(ws, ws_bytes, (size_t)router_stats_ws_bytes(cfg->T, cfg->E));
+  if (st != MOE_OK) return st;
+  RouterStatsLaunch a{logits, bias, gumbel_u, counts, prob_mean, aux, (double*)ws, cfg->T, cfg->E, cfg->score,
+                      cfg->bias_mode, cfg->tau};
+  return launch_router_stats(a, (hipStream_t)stream);
+}
+
+moe_status moe_bias_update(const moe_config* cfg, const int32_t* counts, float* bias, float decay, float rate,
+                           void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  if (!counts || !bias) return fail(MOE_ERR_INVALID_ARGUMENT, "counts and bias must be non-NULL");
+  if (!std::isfinite(decay) || !std::isfinite(rate))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "decay = %g and rate = %g must be finite", (double)decay, (double)rate);
+  return launch_bias_update(counts, bias, cfg->E, decay, rate, (hipStream_t)stream);
 }
 
 moe_status moe_profile_enable(int32_t on) {

@@ -35,6 +35,7 @@
 #include <algorithm>
 
 #include "common.h"
+#include "route_keys.h"
 
 namespace moe {
 namespace {
@@ -93,21 +94,9 @@ __device__ __forceinline__ void route_token(const RouteLaunch& a, int t, int lan
     if (e < E) {
       const float z = zget(e);
       if (a.logits) a.logits[(size_t)t * E + e] = z;
-      if (a.score == MOE_SCORE_SOFTMAX) {
-        float l = z;
-        if (a.bias_mode == MOE_BIAS_LOGIT) l = l + a.bias[e];
-        if (a.gumbel_u) {
-          const double u = (double)a.gumbel_u[(size_t)t * E + e];
-          l = l + (float)(-log(-log(u)));
-        }
-        l = l / tau;
-        basis[i] = l;
-        key[i] = (a.bias_mode == MOE_BIAS_SELECT_ONLY) ? l + a.bias[e] : l;
-      } else {
-        const float s = (float)(1.0 / (1.0 + exp(-(double)z)));
-        basis[i] = s;
-        key[i] = (a.bias_mode == MOE_BIAS_SELECT_ONLY) ? s + a.bias[e] : s;
-      }
+      const KeyBasis kb = key_basis(z, e, (size_t)t * E + e, a.score, a.bias_mode, a.bias, a.gumbel_u, tau);
+      basis[i] = kb.basis;
+      key[i] = kb.key;
     }
   }
 

@@ -112,6 +112,16 @@ def test_entry_points_validate_before_launch(L):
     # forward: workspace too small
     assert lib.moe_forward(ctypes.byref(cfg), dummy, dummy, None, None, ctypes.byref(w), dummy, None,
                            None, dummy, 1024, None) == 3
+    # balancing statistics: counts / prob_mean required, a logit bias needs the vector,
+    # Gumbel noise needs softmax scoring, the partials need workspace
+    assert lib.moe_router_stats(ctypes.byref(cfg), dummy, None, None, None, dummy, None, dummy, big, None) == 1
+    assert lib.moe_router_stats(ctypes.byref(cfgb), dummy, None, None, dummy, dummy, None, dummy, big, None) == 1
+    assert lib.moe_router_stats(ctypes.byref(cfgs), dummy, None, dummy, dummy, dummy, None, dummy, big, None) == 1
+    assert lib.moe_router_stats(ctypes.byref(cfg), dummy, None, None, dummy, dummy, None, dummy, 8, None) == 3
+    assert lib.moe_bias_update(ctypes.byref(cfg), dummy, None, ctypes.c_float(0.99), ctypes.c_float(0.01),
+                               None) == 1
+    assert lib.moe_bias_update(ctypes.byref(cfg), dummy, dummy, ctypes.c_float(float("nan")),
+                               ctypes.c_float(0.01), None) == 1
 
 
 def test_workspace_and_rows(L):

@@ -27,6 +27,8 @@ SMALL = {
     "bf16_skewed_big": WK["mixtral_bf16"].replace(name="bf16z", T=800, d=256, E=8, k=2, F=256,
                                                   bias_mode=W.BIAS_LOGIT, bias_kind="zipf1.2"),
     "skewed_fp8_decode": WK["skewed_fp8_decode"],
+    # decode-sized bf16 batch: the streaming GEMM with half-width blocks
+    "bf16_decode": WK["mixtral_bf16"].replace(name="bf16d", T=64, d=512, E=16, k=2, F=256),
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
