@@ -306,6 +306,84 @@ def permute(idx: np.ndarray, E: int, C: Optional[int]) -> Permutation:
                        src.astype(np.int32), int((counts - kept).sum()))
 
 
+def fallback_candidates(keys: np.ndarray, k: int, depth: int) -> np.ndarray:
+    """The `depth` next-best experts of each token after its top-k, by the same
+    keys and tie rule as the top-k (int32 [T, depth])."""
+    idx, _, _ = topk_by_keys(keys, k + depth)
+    return idx[:, k:]
+
+
+def permute_reroute(idx: np.ndarray, fallback: np.ndarray, E: int, C: Optional[int]) -> Permutation:
+    """S3/S4 with the overflow re-routing of [P2] s3.2 ("Level 2": an overflowed
+    token is not dropped; a fallback router takes its next-best expert that is
+    not full).
+
+    Reading, step by step:
+      1. first pass exactly as permute(): pairs (t, j) ranked per expert in
+         (t, j) order, kept iff rank < C;
+      2. the pairs the first pass dropped are visited in the same (t, j) order;
+         each takes the first expert of its token's fallback list (the next-best
+         experts by key after the top-k, fallback_candidates) that holds fewer
+         than C pairs at that moment and is not already serving the token
+         through an earlier re-routed pair; if there is none it stays dropped;
+      3. a re-routed pair keeps its gate weight (the weights are the routing's;
+         only the expert serving the slot changes);
+      4. expert e's rows are its first-pass pairs in (t, j) order, then its
+         re-routed pairs in (t, j) order.
+    counts stays the requested counts of the first pass; kept and offsets count
+    the final rows; n_dropped the pairs left without an expert.
+    """
+    idx = np.asarray(idx)
+    fb = np.asarray(fallback)
+    T, k = idx.shape
+    base = permute(idx, E, C)
+    if C is None:
+        return base
+    counts = base.counts.astype(np.int64)
+    kept1 = np.minimum(counts, C)
+    rank1 = np.zeros((T, k), dtype=np.int64)
+    seen = np.zeros(E, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            e = int(idx[t, j])
+            rank1[t, j] = seen[e]
+            seen[e] += 1
+    load = kept1.copy()
+    new_e = np.full((T, k), -1, dtype=np.int64)
+    rank2 = np.zeros((T, k), dtype=np.int64)
+    for t in range(T):
+        used = set()
+        for j in range(k):
+            if rank1[t, j] < C:
+                continue
+            for c in fb[t]:
+                c = int(c)
+                if c in used or load[c] >= C:
+                    continue
+                new_e[t, j] = c
+                rank2[t, j] = load[c] - kept1[c]
+                load[c] += 1
+                used.add(c)
+                break
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(load)
+    dest = np.full((T, k), -1, dtype=np.int64)
+    src = np.full(T * k, -1, dtype=np.int64)
+    for t in range(T):
+        for j in range(k):
+            if rank1[t, j] < C:
+                row = offsets[idx[t, j]] + rank1[t, j]
+            elif new_e[t, j] >= 0:
+                c = new_e[t, j]
+                row = offsets[c] + kept1[c] + rank2[t, j]
+            else:
+                continue
+            dest[t, j] = row
+            src[row] = t
+    return Permutation(counts.astype(np.int32), load.astype(np.int32), offsets.astype(np.int32),
+                       dest.astype(np.int32), src.astype(np.int32), int(T * k - load.sum()))
+
+
 # ---------------------------------------------------------------------------
 # S5/S6 expert FFN
 def fp8_e4m3fn_decode(codes: np.ndarray) -> np.ndarray:

@@ -15,7 +15,7 @@ import tests.test_oracle_pins as pins
 _orig = {name: getattr(O, name) for name in
          ["router_logits", "gumbel_noise", "topk_by_keys", "gate_weights", "capacity",
           "permute", "swiglu_ffn", "combine", "fp8_e4m3fn_decode", "selection_keys",
-          "silu", "router_probs", "router_stats", "bias_update"]}
+          "silu", "router_probs", "router_stats", "bias_update", "permute_reroute"]}
 
 
 def m_router_wrong_column(x, w):
@@ -106,6 +106,76 @@ def m_bias_unnormalised_load(bias, counts, decay=0.99, rate=0.01):
     return (decay * np.asarray(bias, np.float64) - rate * np.asarray(counts, np.float64)).astype(np.float32)
 
 
+def _reroute_variant(idx, fallback, E, C, *, check_load=True, distinct=True, reverse=False,
+                     reroute_first=False):
+    """The re-routing rule with one knob turned (a plausible mistake)."""
+    idx = np.asarray(idx)
+    fb = np.asarray(fallback)
+    T, k = idx.shape
+    if C is None:
+        return _orig["permute"](idx, E, C)
+    counts = np.bincount(idx.ravel(), minlength=E).astype(np.int64)
+    kept1 = np.minimum(counts, C)
+    rank1 = np.zeros((T, k), np.int64)
+    seen = np.zeros(E, np.int64)
+    for t in range(T):
+        for j in range(k):
+            rank1[t, j] = seen[idx[t, j]]
+            seen[idx[t, j]] += 1
+    load = kept1.copy()
+    new_e = np.full((T, k), -1)
+    rank2 = np.zeros((T, k), np.int64)
+    order = range(T - 1, -1, -1) if reverse else range(T)
+    for t in order:
+        used = set()
+        for j in range(k):
+            if rank1[t, j] < C:
+                continue
+            for c in fb[t]:
+                c = int(c)
+                if (distinct and c in used) or (check_load and load[c] >= C):
+                    continue
+                new_e[t, j] = c
+                rank2[t, j] = load[c] - kept1[c]
+                load[c] += 1
+                used.add(c)
+                break
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(load)
+    dest = np.full((T, k), -1, np.int64)
+    src = np.full(max(T * k, int(load.sum())), -1, np.int64)
+    for t in range(T):
+        for j in range(k):
+            if rank1[t, j] < C:
+                e = idx[t, j]
+                row = offsets[e] + rank1[t, j] + ((load[e] - kept1[e]) if reroute_first else 0)
+            elif new_e[t, j] >= 0:
+                c = new_e[t, j]
+                row = offsets[c] + (0 if reroute_first else kept1[c]) + rank2[t, j]
+            else:
+                continue
+            dest[t, j] = row
+            src[row] = t
+    return O.Permutation(counts.astype(np.int32), load.astype(np.int32), offsets.astype(np.int32),
+                         dest.astype(np.int32), src[: T * k].astype(np.int32), int(T * k - load.sum()))
+
+
+def m_reroute_ignores_capacity(idx, fb, E, C):
+    return _reroute_variant(idx, fb, E, C, check_load=False)
+
+
+def m_reroute_repeats_expert(idx, fb, E, C):
+    return _reroute_variant(idx, fb, E, C, distinct=False)
+
+
+def m_reroute_last_token_first(idx, fb, E, C):
+    return _reroute_variant(idx, fb, E, C, reverse=True)
+
+
+def m_reroute_rows_before_first_pass(idx, fb, E, C):
+    return _reroute_variant(idx, fb, E, C, reroute_first=True)
+
+
 MUTATIONS = [
     ("router_logits", m_router_wrong_column, ["test_router_unit_vectors_select_rows"]),
     ("gumbel_noise", m_gumbel_sign, ["test_gumbel_statistics_match_gumbel01",
@@ -127,6 +197,12 @@ MUTATIONS = [
     ("router_stats", m_stats_sum_not_mean, ["test_router_stats_hand_example_and_uniform_closed_form"]),
     ("bias_update", m_bias_wrong_sign, ["test_bias_update_hand_examples"]),
     ("bias_update", m_bias_unnormalised_load, ["test_bias_update_hand_examples"]),
+    ("permute_reroute", m_reroute_ignores_capacity, ["test_reroute_hand_example_fills_next_best_free_expert"]),
+    ("permute_reroute", m_reroute_repeats_expert,
+     ["test_reroute_slots_of_one_token_take_distinct_experts_in_key_order"]),
+    ("permute_reroute", m_reroute_last_token_first, ["test_reroute_priority_goes_to_the_earlier_token",
+                                                     "test_reroute_matches_deferred_acceptance_bruteforce"]),
+    ("permute_reroute", m_reroute_rows_before_first_pass, ["test_reroute_rows_follow_the_first_pass"]),
 ]
 
 

@@ -505,3 +505,157 @@ def test_bias_update_hand_examples():
     b3 = O.bias_update(np.array([1.0, -2.0], np.float32), np.array([0, 0]))
     np.testing.assert_allclose(b3, [0.99, -1.98], rtol=0, atol=1e-7)
     assert b.dtype == np.float32
+
+
+# ------------------------------------------------------ overflow re-routing
+def _expert_of_rows(P, idx_shape):
+    """Final expert of every pair, from the offsets and dest_row (-1 = dropped)."""
+    ex = np.full(idx_shape, -1)
+    for t in range(idx_shape[0]):
+        for j in range(idx_shape[1]):
+            r = P.dest_row[t, j]
+            if r >= 0:
+                ex[t, j] = int(np.searchsorted(P.offsets, r, side="right") - 1)
+    return ex
+
+
+def test_reroute_without_overflow_is_the_plain_permutation():
+    r = _rng(21)
+    idx = r.integers(0, 6, (40, 2))
+    fb = np.tile(np.arange(6), (40, 1))[:, :3]
+    for C in (None, 1000):
+        a, b = O.permute_reroute(idx, fb, 6, C), O.permute(idx, 6, C)
+        for f in ("counts", "kept", "offsets", "dest_row", "src_token"):
+            np.testing.assert_array_equal(getattr(a, f), getattr(b, f))
+        assert a.n_dropped == b.n_dropped == 0
+
+
+def test_reroute_hand_example_fills_next_best_free_expert():
+    """Four tokens all pick expert 0 (C = 1), each with fallbacks (1, 2): the first
+    is kept, the second goes to 1, the third finds 1 full and goes to 2, the
+    fourth finds everything full and is dropped."""
+    idx = np.zeros((4, 1), np.int32)
+    fb = np.tile([1, 2], (4, 1))
+    P = O.permute_reroute(idx, fb, 3, 1)
+    np.testing.assert_array_equal(_expert_of_rows(P, idx.shape)[:, 0], [0, 1, 2, -1])
+    np.testing.assert_array_equal(P.counts, [4, 0, 0])
+    np.testing.assert_array_equal(P.kept, [1, 1, 1])
+    assert P.n_dropped == 1
+
+
+def test_reroute_slots_of_one_token_take_distinct_experts_in_key_order():
+    """Token 2's two slots both overflow (C = 2) and share fallbacks (2, 3): the
+    first slot takes 2; expert 2 still has room, but it already serves the
+    token, so the second slot takes 3."""
+    idx = np.array([[0, 1], [0, 1], [0, 1]])
+    fb = np.array([[2, 3], [2, 3], [2, 3]])
+    P = O.permute_reroute(idx, fb, 4, 2)
+    np.testing.assert_array_equal(_expert_of_rows(P, idx.shape), [[0, 1], [0, 1], [2, 3]])
+
+
+def test_reroute_rows_follow_the_first_pass():
+    """Token 2 overflows expert 0 (C = 2) and falls back to expert 1, which kept
+    token 3 in the first pass: expert 1's rows are token 3 (first pass) then
+    token 2 (re-routed), so offsets (0, 2, 4), dest rows 2 and 3."""
+    idx = np.array([[0], [0], [0], [1]])
+    fb = np.array([[1], [1], [1], [0]])
+    P = O.permute_reroute(idx, fb, 2, 2)
+    np.testing.assert_array_equal(_expert_of_rows(P, idx.shape)[:, 0], [0, 0, 1, 1])
+    np.testing.assert_array_equal(P.offsets, [0, 2, 4])
+    np.testing.assert_array_equal(P.dest_row[:, 0], [0, 1, 3, 2])
+    np.testing.assert_array_equal(P.src_token, [0, 1, 3, 2])
+    assert P.n_dropped == 0
+
+
+def test_reroute_priority_goes_to_the_earlier_token():
+    """Tokens 1 and 2 both overflow expert 0 (C = 1) and both want expert 1, which
+    has room for one: token 1 gets it, token 2 falls through to expert 2."""
+    idx = np.array([[0], [0], [0]])
+    fb = np.array([[1, 2], [1, 2], [1, 2]])
+    P = O.permute_reroute(idx, fb, 3, 1)
+    np.testing.assert_array_equal(_expert_of_rows(P, idx.shape)[:, 0], [0, 1, 2])
+
+
+def _deferred_acceptance(idx, fb, E, C):
+    """Independent formulation: every token with overflowed slots proposes down
+    its fallback list until it holds as many experts as it has such slots; every
+    expert keeps the earliest tokens that fit its spare room and rejects the
+    rest; rejected tokens propose further, until nothing is rejected.  With one
+    priority order shared by all experts this reaches the same assignment as the
+    serial rule; a token's experts go to its overflowed slots in list order."""
+    T, k = idx.shape
+    counts = np.bincount(np.asarray(idx).ravel(), minlength=E)
+    rank = np.zeros((T, k), int)
+    seen = np.zeros(E, int)
+    for t in range(T):
+        for j in range(k):
+            rank[t, j] = seen[idx[t, j]]
+            seen[idx[t, j]] += 1
+    room = C - np.minimum(counts, C)
+    slots = [[j for j in range(k) if rank[t, j] >= C] for t in range(T)]
+    ptr = [0] * T
+    held = [set() for _ in range(T)]
+    while True:
+        for t in range(T):
+            while len(held[t]) < len(slots[t]) and ptr[t] < fb.shape[1]:
+                held[t].add(int(fb[t, ptr[t]]))
+                ptr[t] += 1
+        rejected = False
+        for c in range(E):
+            holders = [t for t in range(T) if c in held[t]]
+            for t in holders[room[c]:]:
+                held[t].discard(c)
+                rejected = True
+        if not rejected:
+            break
+    out = np.where(rank < C, idx, -1)
+    for t in range(T):
+        mine = [int(c) for c in fb[t] if int(c) in held[t]]
+        for j, c in zip(slots[t], mine):
+            out[t, j] = c
+    return out
+
+
+def test_reroute_matches_deferred_acceptance_bruteforce():
+    """Random tiny cases: the serial rule and deferred acceptance agree."""
+    r = _rng(22)
+    for trial in range(300):
+        E = int(r.integers(2, 7))
+        k = int(r.integers(1, min(3, E) + 1))
+        D = int(r.integers(1, E - k + 1)) if E > k else 0
+        T = int(r.integers(1, 10))
+        keys = r.standard_normal((T, E)).astype(np.float32)
+        keys[:, 0] += 2.0  # a hot expert, so overflow happens
+        idx, _, _ = O.topk_by_keys(keys, k)
+        fb = O.fallback_candidates(keys, k, D) if D else np.zeros((T, 0), np.int32)
+        C = int(r.integers(1, 4))
+        P = O.permute_reroute(idx, fb, E, C)
+        np.testing.assert_array_equal(_expert_of_rows(P, idx.shape), _deferred_acceptance(idx, fb, E, C),
+                                      err_msg=f"trial {trial}")
+
+
+def test_reroute_invariants_on_skewed_traffic():
+    """Zipf-like traffic: every expert holds at most C rows, a token's experts are
+    distinct, rows and tokens agree, and a pair left dropped found every one of its
+    fallbacks full or already serving its token."""
+    r = _rng(23)
+    T, E, k, D, C = 300, 16, 2, 4, 30
+    keys = (r.standard_normal((T, E)) - 0.6 * np.arange(E)).astype(np.float32)
+    idx, _, _ = O.topk_by_keys(keys, k)
+    fb = O.fallback_candidates(keys, k, D)
+    P = O.permute_reroute(idx, fb, E, C)
+    assert P.kept.max() <= C and P.n_dropped > 0 and P.n_dropped < O.permute(idx, E, C).n_dropped
+    ex = _expert_of_rows(P, idx.shape)
+    full = P.kept >= C
+    for t in range(T):
+        mine = [e for e in ex[t] if e >= 0]
+        assert len(mine) == len(set(mine))
+        for j in range(k):
+            if ex[t, j] < 0:
+                assert all(full[c] or c in mine for c in fb[t])
+    n = int(P.offsets[-1])
+    for t in range(T):
+        for j in range(k):
+            if P.dest_row[t, j] >= 0:
+                assert P.src_token[P.dest_row[t, j]] == t
+    assert (P.src_token[:n] >= 0).all() and (P.src_token[n:] == -1).all()
