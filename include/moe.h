@@ -97,6 +97,9 @@ typedef struct {
   int32_t w_dtype;           /* expert weights: MOE_F32 (requires act F32), MOE_BF16,     */
                              /* MOE_FP8_E4M3FN (requires act BF16)                        */
   int32_t out_dtype;         /* layer output: MOE_F32 or MOE_BF16                         */
+  int32_t reroute_depth;     /* overflow re-routing ([P2] s3.2 level 2): 0 = off, else D  */
+                             /* in 1 .. min(8, E - top_k) fallback experts per token;      */
+                             /* needs top_k <= 64; acts only under a capacity limit        */
 } moe_config;
 
 /* Expert weights.  Scales are required for fp8 and must be NULL otherwise.
@@ -112,7 +115,8 @@ typedef struct {
 /* Optional routing outputs of moe_forward (any member may be NULL). */
 typedef struct {
   float* logits;       /* [T,E] f32 router logits z                                  */
-  int32_t* topk_idx;   /* [T,k] chosen experts, descending key, ties -> lower index   */
+  int32_t* topk_idx;   /* [T,k+D] chosen experts, descending key, ties -> lower index, */
+                       /* then the D = reroute_depth fallback experts               */
   float* topk_w;       /* [T,k] gate weights                                          */
   int32_t* dest_row;   /* [T,k] permuted row of each pair, -1 when dropped            */
 } moe_routing_out;
@@ -146,7 +150,8 @@ moe_status moe_permuted_rows(const moe_config* cfg, int64_t* rows);
  *              ([P2] s5.1); softmax only.  Noise g = -log(-log u) is added to the
  *              (biased) logits before the temperature: l = (z + b + g) / tau.
  *   logits     [T,E] f32 output z, or NULL
- *   topk_idx   [T,k] int32 output;  topk_w [T,k] f32 output
+ *   topk_idx   [T,k+D] int32 output (D = reroute_depth: the next-best experts
+ *              after the top-k, in key order);  topk_w [T,k] f32 output
  *   ws, ws_bytes  device workspace (bf16 x: split router weights and logit
  *              partials; fp32 x needs none and may pass NULL) */
 moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router,
@@ -158,7 +163,7 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router
  * routing -- the tensor reorganised by routing index).  Pairs (t,j) are ranked
  * per expert in (t,j) order; a pair is kept iff its rank < C.  Kept pairs of
  * expert e occupy rows offsets[e] .. offsets[e+1]-1 in token order.
- *   x          [T,d] act_dtype;  topk_idx [T,k] int32 in [0,E)
+ *   x          [T,d] act_dtype;  topk_idx [T,k+D] int32 in [0,E)
  *   counts     [E]   int32 out: pairs routed to each expert (before the limit)
  *   offsets    [E+1] int32 out: exclusive scan of kept = min(counts, C)
  *   dest_row   [T,k] int32 out: row of each pair, -1 when dropped
@@ -166,6 +171,17 @@ moe_status moe_route(const moe_config* cfg, const void* x, const float* w_router
  *   n_dropped  [1]   int32 out
  *   x_perm     [R,d] act_dtype out: x_perm[dest_row[t,j]] = x[t]
  *   (R = moe_permuted_rows(cfg)); ws, ws_bytes: device workspace */
+/* Overflow re-routing (reroute_depth = D > 0 with a capacity limit; [P2] s3.2
+ * level 2: an overflowed token goes to its next-best expert that is not full):
+ * topk_idx then has k + D columns, the top-k followed by the D next-best
+ * experts in key order (moe_route writes them).  After the first pass, the
+ * dropped pairs are visited in (t,j) order and each takes the first of its
+ * token's D fallback experts that holds fewer than C pairs and does not already
+ * serve the token; none -> it stays dropped.  A re-routed pair keeps its gate
+ * weight.  Expert e's rows: its first-pass pairs in (t,j) order, then its
+ * re-routed pairs in (t,j) order.  counts stay the requested counts; offsets
+ * (and moe_forward's kept) count the final rows; n_dropped the pairs left
+ * without an expert. */
 moe_status moe_permute(const moe_config* cfg, const void* x, const int32_t* topk_idx,
                        int32_t* counts, int32_t* offsets, int32_t* dest_row,
                        int32_t* src_token, int32_t* n_dropped, void* x_perm,
@@ -196,7 +212,8 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const float* 
 
 /* The whole layer ([P5] fused MoE forward: hidden states, router, experts ->
  * output).  Intermediates live in the workspace.
- *   stats    [2E+1] int32 out, or NULL: counts[E], kept[E], n_dropped
+ *   stats    [2E+1] int32 out, or NULL: counts[E] (requested), kept[E] (final rows
+ *            per expert, re-routed pairs included), n_dropped
  *   routing  optional copies of the routing decision, or NULL */
 moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_router,
                        const float* bias, const float* gumbel_u,

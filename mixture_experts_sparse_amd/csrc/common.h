@@ -79,6 +79,7 @@ struct RouteLaunch {
   int T, d, E, k, score, renormalize, bias_mode, act_dtype;
   float tau;
   // bf16 path: padded expert count, d-split, and workspace buffers
+  int fb = 0;               // fallback experts written after the top-k (topk_idx has k + fb columns)
   int ep = 0, split = 0;
   uint16_t* wt = nullptr;   // [3][ep][d] split router weights
   float* part = nullptr;    // [split][T][ep] logit partials
@@ -99,6 +100,8 @@ struct PermuteLaunch {
   int T, d, E, k, act_bytes;
   int64_t capacity;      // < 0: no limit
   int64_t rows;          // permuted rows provided by the caller
+  int fb = 0;            // fallback experts per token after the top-k (topk_idx has k + fb columns)
+  int32_t* reroute = nullptr;  // workspace [2 T k + E + 1] for re-routing (fb > 0 with a limit)
 };
 moe_status launch_permute(const PermuteLaunch& a, hipStream_t s);
 

@@ -121,10 +121,17 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "w_dtype = %d", c->w_dtype);
   }
   if (c->d % 128) return fail(MOE_ERR_UNSUPPORTED, "d = %d must be a multiple of 128", c->d);
+  if (c->reroute_depth < 0 || c->reroute_depth > std::min(8, c->E - c->top_k))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "reroute_depth = %d outside [0, min(8, E - top_k)]", c->reroute_depth);
+  if (c->reroute_depth > 0 && c->top_k > 64)
+    return fail(MOE_ERR_UNSUPPORTED, "overflow re-routing needs top_k <= 64");
   return MOE_OK;
 }
 
 // C = max(1, floor(T*k/E*cf)) in double from the float32 factor; -1 = no limit.
+static_assert(sizeof(moe_config) == 15 * 4, "moe_config layout is part of the ABI");
+static_assert(sizeof(moe_expert_weights) == 12 * 8, "moe_expert_weights layout is part of the ABI");
+
 int64_t capacity_of(const moe_config* c) {
   if (!(c->capacity_factor > 0.f)) return -1;
   const double v = std::floor((double)c->T * (double)c->top_k / (double)c->E * (double)c->capacity_factor);
@@ -146,7 +153,7 @@ struct Layout {
   int route_ep, route_split;
   size_t route_wt, route_part, route_end;
   // permute / ffn scratch
-  size_t hist, tiles, tiles_sh, h, h_sh;
+  size_t hist, reroute, tiles, tiles_sh, h, h_sh;
   int split, split_sh;          // K splits of the routed / shared down passes
   size_t y_rest, y_sh_rest;     // partial sums 1.. of y_perm / y_shared
   // forward intermediates
@@ -174,6 +181,7 @@ Layout layout_of(const moe_config* c) {
   // scratch shared by moe_permute and moe_expert_ffn (they never run concurrently
   // on one workspace within moe_forward; standalone callers pass one each)
   L.hist = take(sizeof(int32_t) * nblk * c->E);
+  L.reroute = take(c->reroute_depth > 0 ? sizeof(int32_t) * (2 * (size_t)P + c->E + 1) : 0);
   L.perm_end = o;
   L.tiles = take(sizeof(int32_t) * 2 * (c->E + 1));
   L.tiles_sh = take(sizeof(int32_t) * 4);
@@ -186,7 +194,7 @@ Layout layout_of(const moe_config* c) {
   L.ffn_end = o;
   o = std::max(L.ffn_end, L.route_end);
   L.logits = take(sizeof(float) * (size_t)c->T * c->E);
-  L.idx = take(sizeof(int32_t) * P);
+  L.idx = take(sizeof(int32_t) * (size_t)c->T * (c->top_k + c->reroute_depth));
   L.w = take(sizeof(float) * P);
   L.counts = take(sizeof(int32_t) * c->E);
   L.offsets = take(sizeof(int32_t) * (c->E + 1));
@@ -249,6 +257,7 @@ moe_status run_route(const moe_config* c, const void* x, const float* w_router, 
   RouteLaunch r{x, w_router, bias, gumbel_u, logits, topk_idx, topk_w, c->T, c->d, c->E, c->top_k,
                 c->score, c->renormalize, c->bias_mode, c->act_dtype, c->tau};
   const Layout L = layout_of(c);
+  r.fb = c->reroute_depth;
   r.ep = L.route_ep;
   r.split = L.route_split;
   r.wt = (uint16_t*)(ws + L.route_wt);
@@ -263,6 +272,8 @@ moe_status run_permute(const moe_config* c, const void* x, const int32_t* topk_i
   PermuteLaunch p{x, topk_idx, counts, offsets, dest_row, src_token, n_dropped, x_perm, stats,
                   (int32_t*)(ws + L.hist), c->T, c->d, c->E, c->top_k, dtype_bytes(c->act_dtype),
                   capacity_of(c), perm_rows(c)};
+  p.fb = c->reroute_depth;
+  p.reroute = (int32_t*)(ws + L.reroute);
   return launch_permute(p, s);
 }
 

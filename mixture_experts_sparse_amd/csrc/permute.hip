@@ -23,15 +23,21 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// expert of pair p = t k + j; the index matrix has ld >= k columns per token
+__device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, int p, int k, int ld) {
+  return idx[(size_t)(p / k) * ld + (p % k)];
+}
+
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx,
-                                                        int32_t* __restrict__ hist, int P, int E) {
+                                                        int32_t* __restrict__ hist, int P, int E, int k,
+                                                        int ld) {
   __shared__ int h[256];
   for (int e = threadIdx.x; e < E; e += kThreads) h[e] = 0;
   __syncthreads();
   const int p0 = blockIdx.x * kPermChunk;
   const int p1 = min(p0 + kPermChunk, P);
   for (int p = p0 + threadIdx.x; p < p1; p += kThreads) {
-    const int e = idx[p];
+    const int e = pair_expert(idx, p, k, ld);
     if (e >= 0 && e < E) atomicAdd(&h[e], 1);  // ids outside [0,E) are ignored
   }
   __syncthreads();
@@ -86,7 +92,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ dest_row,
                                                         int32_t* __restrict__ src_token,
-                                                        int P, int E, int k, int64_t cap,
+                                                        int P, int E, int k, int ld, int64_t cap,
                                                         int64_t rows) {
   __shared__ int running[256];
   __shared__ int wcnt[4][256];
@@ -102,7 +108,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r0 = p0; r0 < p1; r0 += kThreads) {  // uniform trip count in the block
     const int p = r0 + tid;
-    const int e_in = (p < p1) ? idx[p] : -1;
+    const int e_in = (p < p1) ? pair_expert(idx, p, k, ld) : -1;
     const bool valid = e_in >= 0 && e_in < E;  // ids outside [0,E) are dropped uncounted
     const int e = valid ? e_in : 0;
     if (p < p1 && !valid) dest_row[p] = -1;
@@ -139,6 +145,183 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
   // whichever block owns the pair, and are < n_rows, so the writes are disjoint)
   for (int64_t r = (int64_t)p0 + tid; r < (int64_t)p0 + kPermChunk && r < rows; r += kThreads)
     if (r >= n_rows) src_token[r] = -1;
+}
+
+// Overflow re-routing (page "Parameter scale and the truth about sparse
+// activation" (deepseek.csdn.net), s3.2 level 2: an overflowed token goes to
+// its next-best expert that is not full).  The serial rule -- dropped pairs in
+// (t, j) order, each taking the first of its token's D fallback experts that is
+// below capacity and not already serving the token -- is computed by one wave
+// over chunks of whole tokens in order.  Inside a chunk the lanes settle by
+// deferred acceptance: every unsettled lane proposes its next fallback, a lane
+// loses an expert to an earlier lane of its own token, or when its rank among
+// the lanes holding that expert reaches the expert's remaining room, and losers
+// propose again until no lane loses.  All experts rank lanes in the same (t, j)
+// order, so this reaches exactly the serial assignment; the chunk's winners then
+// use up their experts' room before the next chunk starts.
+//   out: re_e[p] (fallback expert or -1), re_rank[p] (rank among the expert's
+//   re-routed pairs), off_first (the first pass's offsets), offsets (final),
+//   stats kept / n_dropped (final)
+// A chunk's inputs, loaded one chunk ahead so the sequential walk never waits
+// on memory: the pair's routed expert, its first-pass row and its token's D
+// fallback experts (ids outside [0,E) from a caller count as no candidate).
+struct RerouteLane {
+  int e, d;
+  int f0, f1, f2, f3, f4, f5, f6, f7;  // named, not an array: kept in registers
+};
+
+__device__ __forceinline__ RerouteLane load_lane(const int32_t* __restrict__ idx, const int32_t* __restrict__ dest_row,
+                                                 int ld, int k, int D, int T, int lanes, int t0, int lane) {
+  RerouteLane v;
+  const int t = t0 + lane / k, j = lane % k;
+  const bool active = lane < lanes && t < T;
+  v.e = active ? idx[(size_t)t * ld + j] : -1;
+  v.d = active ? dest_row[(size_t)t * k + j] : 0;
+  const int32_t* f = idx + (size_t)t * ld + k;
+  v.f0 = (active && 0 < D) ? f[0] : -1;
+  v.f1 = (active && 1 < D) ? f[1] : -1;
+  v.f2 = (active && 2 < D) ? f[2] : -1;
+  v.f3 = (active && 3 < D) ? f[3] : -1;
+  v.f4 = (active && 4 < D) ? f[4] : -1;
+  v.f5 = (active && 5 < D) ? f[5] : -1;
+  v.f6 = (active && 6 < D) ? f[6] : -1;
+  v.f7 = (active && 7 < D) ? f[7] : -1;
+  return v;
+}
+
+// drop the first fallback: the list moves up one place (the walk only ever
+// advances, so the current candidate is always f0 -- no indexed access)
+__device__ __forceinline__ void advance(RerouteLane& v) {
+  v.f0 = v.f1; v.f1 = v.f2; v.f2 = v.f3; v.f3 = v.f4;
+  v.f4 = v.f5; v.f5 = v.f6; v.f6 = v.f7; v.f7 = -1;
+}
+
+__global__ __launch_bounds__(64) void reroute_kernel(const int32_t* __restrict__ idx, int ld, int k, int D,
+                                                     int T, int E, int cap, const int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ off_first,
+                                                     const int32_t* __restrict__ dest_row,
+                                                     int32_t* __restrict__ re_e, int32_t* __restrict__ re_rank,
+                                                     int32_t* __restrict__ n_dropped, int32_t* __restrict__ stats) {
+  __shared__ int room[256];
+  __shared__ int given[256];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < 256; e += 64) {
+    room[e] = e < E ? cap - min(counts[e], cap) : 0;
+    given[e] = 0;
+  }
+  for (int e = lane; e <= E; e += 64) off_first[e] = offsets[e];
+  __syncthreads();
+  const int tpc = 64 / k;      // whole tokens per chunk
+  const int lanes = tpc * k;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const uint64_t tok = (k == 64 ? ~0ull : ((1ull << k) - 1)) << ((lane / k) * k);  // my token's lanes
+  RerouteLane nxt = load_lane(idx, dest_row, ld, k, D, T, lanes, 0, lane);
+  for (int t0 = 0; t0 < T; t0 += tpc) {
+    const RerouteLane cur_in = nxt;
+    if (t0 + tpc < T) nxt = load_lane(idx, dest_row, ld, k, D, T, lanes, t0 + tpc, lane);
+    const int t = t0 + lane / k, j = lane % k;
+    const bool active = lane < lanes && t < T;
+    const int p = t * k + j;
+    const bool over = active && cur_in.e >= 0 && cur_in.e < E && cur_in.d < 0;
+    if (active) re_e[p] = -1;
+    if (__ballot(over) == 0) continue;
+    RerouteLane fl = cur_in;
+    int ptr = 0, cur = -1;
+    uint64_t same = 0;  // lanes proposing my expert in the last round
+    // every round a lane either keeps its expert or moves on down its list, and
+    // a list has D entries: the loop ends after at most lanes * D + 1 rounds
+    for (;;) {
+      // next candidate; an expert without room at the chunk's start cannot take
+      // the lane (room only shrinks within the chunk), so it is skipped at once
+      while (over && cur < 0 && ptr < D) {
+        const int cand = fl.f0;
+        if (cand >= 0 && cand < E && room[cand] > 0) {
+          cur = cand;
+        } else {
+          ++ptr;
+          advance(fl);
+        }
+      }
+      const bool prop = over && cur >= 0;
+      const int c = prop ? cur : 0;
+      same = __ballot(prop);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint64_t ones = __ballot(prop && ((c >> b) & 1));
+        same &= ((c >> b) & 1) ? ones : ~ones;
+      }
+      const bool dup = prop && (same & tok & lt) != 0;  // an earlier slot of my token has it
+      const bool hold = prop && !dup;
+      const uint64_t holders = same & __ballot(hold);   // lanes keeping the same expert
+      const bool lose = dup || (hold && __popcll(holders & lt) >= room[c]);
+      if (__ballot(lose) == 0) break;
+      if (lose) {
+        cur = -1;
+        ++ptr;
+        advance(fl);
+      }
+    }
+    // commit the chunk (the last round rejected nobody, so every proposing lane
+    // won and `same` is the set of winners of my expert): winners take their
+    // rank among the expert's re-routed pairs; the last one books the room
+    const bool won = over && cur >= 0;
+    const int c = won ? cur : 0;
+    const uint64_t peers = won ? same : 0ull;
+    const int r = __popcll(peers & lt), h = __popcll(peers);
+    if (won) {
+      re_e[p] = c;
+      re_rank[p] = given[c] + r;
+    }
+    __syncthreads();
+    if (won && r == h - 1) {
+      given[c] += h;
+      room[c] -= h;
+    }
+    __syncthreads();
+  }
+  // final rows per expert, their exclusive scan, and the pairs left dropped
+  __shared__ int kept_f[256];
+  for (int e = lane; e < 256; e += 64) kept_f[e] = e < E ? min(counts[e], cap) + given[e] : 0;
+  __syncthreads();
+  if (lane == 0) {
+    int run = 0, req = 0;
+    for (int e = 0; e < E; ++e) {
+      offsets[e] = run;
+      run += kept_f[e];
+      req += counts[e];
+      if (stats) stats[E + e] = kept_f[e];
+    }
+    offsets[E] = run;
+    n_dropped[0] = req - run;
+    if (stats) stats[2 * E] = req - run;
+  }
+}
+
+// Moves every pair to its final row once the re-routed pairs have been placed:
+// first-pass pairs keep their rank within the expert, re-routed pairs follow
+// the expert's first-pass rows.
+__global__ __launch_bounds__(kThreads) void relocate_kernel(const int32_t* __restrict__ idx, int ld, int k, int E,
+                                                            int cap, const int32_t* __restrict__ counts,
+                                                            const int32_t* __restrict__ off_first,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ dest_row,
+                                                            const int32_t* __restrict__ re_e,
+                                                            const int32_t* __restrict__ re_rank,
+                                                            int32_t* __restrict__ src_token, int P) {
+  const int p = blockIdx.x * kThreads + threadIdx.x;
+  if (p >= P) return;
+  const int e = pair_expert(idx, p, k, ld);
+  if (e < 0 || e >= E) return;  // ignored ids stay -1
+  const int d = dest_row[p];
+  int row = -1;
+  if (d >= 0) {
+    row = offsets[e] + (d - off_first[e]);
+  } else {
+    const int c = re_e[p];
+    if (c >= 0) row = offsets[c] + min(counts[c], cap) + re_rank[p];
+  }
+  dest_row[p] = row;
+  if (row >= 0) src_token[row] = p / k;
 }
 
 // One wave per token: the row is read once (16-byte vectors, four per lane in
@@ -194,8 +377,9 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
                        a.stats, a.E);
     return end_launch(tok, s);
   }
+  const int ld = a.k + a.fb;
   int tok = begin_launch("permute_hist", s);
-  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, P, a.E);
+  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, P, a.E, a.k, ld);
   moe_status st = end_launch(tok, s);
   if (st != MOE_OK) return st;
 
@@ -207,9 +391,27 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
 
   tok = begin_launch("permute_rank", s);
   hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, a.offsets,
-                     a.dest_row, a.src_token, P, a.E, a.k, a.capacity, a.rows);
+                     a.dest_row, a.src_token, P, a.E, a.k, ld, a.capacity, a.rows);
   st = end_launch(tok, s);
   if (st != MOE_OK) return st;
+
+  if (a.fb > 0 && a.capacity >= 0) {
+    int32_t* re_e = a.reroute;
+    int32_t* re_rank = re_e + P;
+    int32_t* off_first = re_rank + P;
+    tok = begin_launch("permute_reroute", s);
+    hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(64), 0, s, a.topk_idx, ld, a.k, a.fb, a.T, a.E,
+                       (int)a.capacity, a.counts, a.offsets, off_first, a.dest_row, re_e, re_rank, a.n_dropped,
+                       a.stats);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+    tok = begin_launch("permute_relocate", s);
+    hipLaunchKernelGGL(relocate_kernel, dim3((unsigned)ceil_div(P, kThreads)), dim3(kThreads), 0, s, a.topk_idx,
+                       ld, a.k, a.E, (int)a.capacity, a.counts, off_first, a.offsets, a.dest_row, re_e, re_rank,
+                       a.src_token, P);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+  }
 
   if (!a.x_perm) return MOE_OK;
   const int vec_per_row = a.d * a.act_bytes / 16;

@@ -105,7 +105,8 @@ __device__ __forceinline__ void route_token(const RouteLaunch& a, int t, int lan
   float sel_b[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) { sel_e[s] = 0; sel_b[s] = 0.f; }
-  for (int j = 0; j < a.k; ++j) {
+  // k + fb rounds: the top-k, then the fallback experts for overflow re-routing
+  for (int j = 0; j < a.k + a.fb; ++j) {
     Cand c{-FLT_MAX, 0.f, INT32_MAX};
 #pragma unroll
     for (int i = 0; i < EPL; ++i) {
@@ -166,10 +167,8 @@ __device__ __forceinline__ void route_token(const RouteLaunch& a, int t, int lan
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
     const int j = lane + 64 * s;
-    if (j < a.k) {
-      a.topk_idx[(size_t)t * a.k + j] = sel_e[s];
-      a.topk_w[(size_t)t * a.k + j] = (float)w[s];
-    }
+    if (j < a.k + a.fb) a.topk_idx[(size_t)t * (a.k + a.fb) + j] = sel_e[s];
+    if (j < a.k) a.topk_w[(size_t)t * a.k + j] = (float)w[s];
   }
 }
 

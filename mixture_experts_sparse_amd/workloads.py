@@ -56,6 +56,7 @@ class MoEShape:
     bias_kind: str = "none"     # "none" | "normal0.5" | "zipf1.2"
     seed: int = 1234
     out_dtype: int = DT_F32
+    reroute_depth: int = 0      # overflow re-routing: fallback experts per token (0 = off)
 
     def replace(self, **kw) -> "MoEShape":
         return dataclasses.replace(self, **kw)
@@ -86,6 +87,10 @@ WORKLOADS: Dict[str, MoEShape] = {
     "skewed_fp8": MoEShape("skewed_fp8", T=16384, d=4096, E=128, k=2, F=1536,
                            bias_mode=BIAS_LOGIT, bias_kind="zipf1.2",
                            capacity_factor=1.25, w_dtype=DT_FP8, seed=1238),
+    # the skewed layer with overflow re-routing to the four next-best experts
+    "skewed_fp8_reroute": MoEShape("skewed_fp8_reroute", T=16384, d=4096, E=128, k=2, F=1536,
+                                   bias_mode=BIAS_LOGIT, bias_kind="zipf1.2", capacity_factor=1.25,
+                                   w_dtype=DT_FP8, seed=1238, reroute_depth=4),
     # the same layer at decode size (weight-streaming bound)
     "skewed_fp8_decode": MoEShape("skewed_fp8_decode", T=32, d=4096, E=128, k=2,
                                   F=1536, bias_mode=BIAS_LOGIT, bias_kind="zipf1.2",

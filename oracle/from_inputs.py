@@ -24,7 +24,8 @@ def layer_spec(shape) -> O.LayerSpec:
     """The layer as the C ABI receives it: tau and the capacity factor are float32 there."""
     return O.LayerSpec(shape.T, shape.d, shape.E, shape.k, shape.F, shape.n_shared,
                        shape.score, shape.renormalize, float(np.float32(shape.tau)),
-                       shape.bias_mode, float(np.float32(shape.capacity_factor)))
+                       shape.bias_mode, float(np.float32(shape.capacity_factor)),
+                       shape.reroute_depth)
 
 
 def expert_weights(inp, experts=None) -> O.ExpertWeights:

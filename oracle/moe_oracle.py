@@ -187,14 +187,17 @@ class Routing:
     keys: np.ndarray       # [T,E] float32
     gap_sel: np.ndarray    # [T] float64
     gap_ord: np.ndarray    # [T] float64
+    fallback: Optional[np.ndarray] = None  # [T,depth] int32 next-best experts, or None
 
 
-def route_from_logits(z, rc: RouteConfig, bias=None, u=None) -> Routing:
-    """S2 on given float32 logits: keys -> top-k -> gate weights."""
+def route_from_logits(z, rc: RouteConfig, bias=None, u=None, depth: int = 0) -> Routing:
+    """S2 on given float32 logits: keys -> top-k -> gate weights (and the
+    `depth` fallback experts for overflow re-routing)."""
     keys, basis = selection_keys(z, rc, bias, u)
     idx, gs, go = topk_by_keys(keys, rc.k)
     w = gate_weights(basis, idx, rc)
-    return Routing(idx, w, keys, gs, go)
+    fb = fallback_candidates(keys, rc.k, depth) if depth else None
+    return Routing(idx, w, keys, gs, go, fb)
 
 
 # ---------------------------------------------------------------------------
@@ -500,6 +503,7 @@ class LayerSpec:
     tau: float = 1.0
     bias_mode: int = BIAS_NONE
     capacity_factor: float = 0.0
+    reroute_depth: int = 0
 
     @property
     def route(self) -> RouteConfig:
@@ -530,8 +534,11 @@ def forward(spec: LayerSpec, x, w_router, ew: ExpertWeights, shared: Optional[Ex
     x64 = np.asarray(x, dtype=np.float64)
     z = router_logits(x, w_router)
     if routing is None:
-        routing = route_from_logits(z, spec.route, bias, u)
-    perm = permute(routing.idx, spec.E, spec.C)
+        routing = route_from_logits(z, spec.route, bias, u, spec.reroute_depth)
+    if spec.reroute_depth:
+        perm = permute_reroute(routing.idx, routing.fallback, spec.E, spec.C)
+    else:
+        perm = permute(routing.idx, spec.E, spec.C)
     n = int(perm.offsets[spec.E])
     x_perm = x64[perm.src_token[:n]]
     y_perm = expert_outputs(x_perm, perm.offsets, ew)
@@ -541,6 +548,13 @@ def forward(spec: LayerSpec, x, w_router, ew: ExpertWeights, shared: Optional[Ex
         y_sh = swiglu_ffn(x64, wg, wu, wd)
     out = combine(y_perm, perm.dest_row, routing.w, y_sh)
     return LayerResult(z, routing, perm, x_perm, y_perm, y_sh, out)
+
+
+def serving_experts(perm: Permutation) -> np.ndarray:
+    """The expert whose rows hold each pair (-1 when dropped), from the offsets:
+    the routed expert, or the fallback expert of a re-routed pair."""
+    ex = np.searchsorted(perm.offsets, perm.dest_row, side="right") - 1
+    return np.where(perm.dest_row >= 0, ex, -1).astype(np.int32)
 
 
 def token_outputs(tokens, x, dest_row, idx, w, ew: ExpertWeights,

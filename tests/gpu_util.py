@@ -69,7 +69,7 @@ def run_forward(inp: W.MoEInputs, out_dtype=W.DT_F32, ws=None):
     out = torch.empty((T, d), dtype=torch.float32 if out_dtype == W.DT_F32 else torch.bfloat16, device=dev)
     stats = torch.empty(2 * E + 1, dtype=torch.int32, device=dev)
     routing = {"logits": torch.empty((T, E), dtype=torch.float32, device=dev),
-               "topk_idx": torch.empty((T, k), dtype=torch.int32, device=dev),
+               "topk_idx": torch.empty((T, k + sh.reroute_depth), dtype=torch.int32, device=dev),
                "topk_w": torch.empty((T, k), dtype=torch.float32, device=dev),
                "dest_row": torch.empty((T, k), dtype=torch.int32, device=dev)}
     if ws is None:
@@ -95,7 +95,7 @@ def run_stages(inp: W.MoEInputs, out_dtype=W.DT_F32):
     R = lib.permuted_rows(cfg)
     ws = lib.alloc_workspace(cfg, dev)
     logits = torch.empty((T, E), dtype=torch.float32, device=dev)
-    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    idx = torch.empty((T, k + sh.reroute_depth), dtype=torch.int32, device=dev)
     w = torch.empty((T, k), dtype=torch.float32, device=dev)
     lib.moe_route(cfg, inp.x, inp.w_router, inp.bias, inp.gumbel_u, logits, idx, w, ws)
     counts = torch.empty(E, dtype=torch.int32, device=dev)
@@ -130,17 +130,25 @@ def check_routing(inp: W.MoEInputs, g: dict, report: dict):
     z_ora = O.router_logits(to_np(inp.x), to_np(inp.w_router))
     report["z_err"] = rel_err_scaled(g["logits"], z_ora)
     assert report["z_err"] <= TOL_Z, report
-    r = O.route_from_logits(g["logits"], spec.route, to_np(inp.bias), to_np(inp.gumbel_u))
+    D = sh.reroute_depth
+    r = O.route_from_logits(g["logits"], spec.route, to_np(inp.bias), to_np(inp.gumbel_u), D)
     sel_tie = r.gap_sel < NEAR_TIE
     ord_tie = r.gap_ord < NEAR_TIE
     report["near_tie_sel"] = int(sel_tie.sum())
     report["near_tie_ord"] = int(ord_tie.sum())
     ok = ~sel_tie
-    gs = np.sort(g["topk_idx"], axis=1)
+    g_idx = g["topk_idx"][:, : sh.k]
+    if D:
+        # fallback experts, in order, away from near-ties among the first k + D + 1 keys
+        srt = -np.sort(-r.keys.astype(np.float64), axis=1)[:, : min(sh.k + D + 1, sh.E)]
+        fb_tie = np.min(srt[:, :-1] - srt[:, 1:], axis=1) < NEAR_TIE
+        report["near_tie_fallback"] = int(fb_tie.sum())
+        assert np.array_equal(g["topk_idx"][~fb_tie, sh.k:], r.fallback[~fb_tie]), "fallback experts differ"
+    gs = np.sort(g_idx, axis=1)
     os_ = np.sort(r.idx, axis=1)
     assert np.array_equal(gs[ok], os_[ok]), "expert sets differ away from near-ties"
     ok2 = ok & ~ord_tie
-    assert np.array_equal(g["topk_idx"][ok2], r.idx[ok2]), "expert order differs away from near-ties"
+    assert np.array_equal(g_idx[ok2], r.idx[ok2]), "expert order differs away from near-ties"
     if ok2.any():
         report["w_err"] = rel_err_scaled(g["topk_w"][ok2], r.w[ok2])
         assert report["w_err"] <= TOL_W, report
@@ -153,8 +161,12 @@ def check_routing(inp: W.MoEInputs, g: dict, report: dict):
 
 
 def check_permutation(sh: W.MoEShape, g: dict, report: dict):
-    """The oracle's permutation of the GPU's indices equals the GPU's, bit for bit."""
-    P = O.permute(g["topk_idx"], sh.E, oracle_capacity(sh))
+    """The oracle's permutation of the GPU's indices (and, with re-routing, the
+    GPU's fallback experts) equals the GPU's, bit for bit."""
+    if sh.reroute_depth:
+        P = O.permute_reroute(g["topk_idx"][:, : sh.k], g["topk_idx"][:, sh.k:], sh.E, oracle_capacity(sh))
+    else:
+        P = O.permute(g["topk_idx"], sh.E, oracle_capacity(sh))
     assert np.array_equal(g["counts"], P.counts)
     assert np.array_equal(g["dest_row"], P.dest_row)
     assert g["n_dropped"] == P.n_dropped

@@ -35,7 +35,7 @@ def test_fullsize_forward(name):
         toks.append(int(dropped_all[0]))
     toks = np.array(sorted(toks))
     shared = FI.shared_weights(inp)
-    ora = O.token_outputs(toks, G.to_np(inp.x), f["dest_row"], f["topk_idx"], f["topk_w"],
+    ora = O.token_outputs(toks, G.to_np(inp.x), f["dest_row"], O.serving_experts(P), f["topk_w"],
                           FI.expert_weights(inp, experts="lazy"), shared)
     rep["out_err_sampled"] = G.out_err(f["out"][toks], ora)
     rep["tokens"] = toks.tolist()

@@ -29,6 +29,19 @@ SMALL = {
     "skewed_fp8_decode": WK["skewed_fp8_decode"],
     # decode-sized bf16 batch: the streaming GEMM with half-width blocks
     "bf16_decode": WK["mixtral_bf16"].replace(name="bf16d", T=64, d=512, E=16, k=2, F=256),
+    # overflow re-routing: fp8 skewed (streaming GEMM), bf16 Zipf (large-tile GEMM),
+    # k = 8 sigmoid, odd k = 3, decode size (C = 1), fp32
+    "reroute_fp8": W.shrink(WK["skewed_fp8"], T=700, d=256, F=256).replace(reroute_depth=4),
+    "reroute_bf16_big": WK["mixtral_bf16"].replace(name="rrb", T=1000, d=256, E=8, k=2, F=256,
+                                                   bias_mode=W.BIAS_LOGIT, bias_kind="zipf1.2",
+                                                   capacity_factor=1.0, reroute_depth=3),
+    "reroute_k8": WK["fine_shared_bf16"].replace(name="rr8", T=300, d=256, E=64, k=8, F=128,
+                                                 capacity_factor=1.0, reroute_depth=4),
+    "reroute_k3": WK["mixtral_bf16"].replace(name="rr3", T=200, d=128, E=16, k=3, F=128,
+                                             bias_mode=W.BIAS_LOGIT, bias_kind="zipf1.2",
+                                             capacity_factor=1.0, reroute_depth=2),
+    "reroute_decode": WK["skewed_fp8_decode"].replace(reroute_depth=8),
+    "reroute_f32": WK["tiny_fp32"].replace(name="rrf", capacity_factor=0.75, reroute_depth=2),
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
@@ -93,7 +106,9 @@ def test_forward_matches_oracle_and_stages(name, dev):
     ora = FI.forward(inp)
     rep = {}
     sel_tie = ora.routing.gap_sel < G.NEAR_TIE
-    same = np.all(np.sort(ora.routing.idx, 1) == np.sort(f["topk_idx"], 1), axis=1)
+    same = np.all(np.sort(ora.routing.idx, 1) == np.sort(f["topk_idx"][:, : sh.k], 1), axis=1)
+    if sh.reroute_depth:  # the fallback experts decide re-routed rows too
+        same &= np.all(ora.routing.fallback == f["topk_idx"][:, sh.k:], axis=1)
     rep["near_tie_sel"] = int(sel_tie.sum())
     rep["flips"] = int((~same).sum())
     assert np.all(same | sel_tie)

@@ -659,3 +659,25 @@ def test_reroute_invariants_on_skewed_traffic():
             if P.dest_row[t, j] >= 0:
                 assert P.src_token[P.dest_row[t, j]] == t
     assert (P.src_token[:n] >= 0).all() and (P.src_token[n:] == -1).all()
+
+
+def test_rerouted_layer_serves_each_slot_by_its_fallback_expert():
+    """A whole layer with re-routing: every kept slot's output row is its serving
+    expert's FFN of the token (token_outputs, one token at a time, with the
+    serving experts), re-routing keeps more pairs than plain dropping, and a
+    dropped slot contributes nothing."""
+    r = _rng(24)
+    T, d, F, E, k = 40, 8, 6, 6, 2
+    x = r.standard_normal((T, d)).astype(np.float32)
+    wr = r.standard_normal((d, E)).astype(np.float32)
+    wr[:, 0] += 2.0  # a hot expert
+    ew = _rand_experts(r, E, d, F)
+    spec = O.LayerSpec(T, d, E, k, F, capacity_factor=1.0, reroute_depth=3)
+    res = O.forward(spec, x, wr, ew)
+    plain = O.forward(O.LayerSpec(T, d, E, k, F, capacity_factor=1.0), x, wr, ew)
+    assert res.perm.n_dropped < plain.perm.n_dropped
+    serving = O.serving_experts(res.perm)
+    assert (serving != res.routing.idx).any()  # some slot moved
+    toks = list(range(T))
+    got = O.token_outputs(toks, x, res.perm.dest_row, serving, res.routing.w, ew)
+    np.testing.assert_allclose(got, res.out, rtol=1e-12, atol=1e-12)
