@@ -57,6 +57,8 @@ class MoEShape:
     seed: int = 1234
     out_dtype: int = DT_F32
     reroute_depth: int = 0      # overflow re-routing: fallback experts per token (0 = off)
+    n_groups: int = 0           # group-limited routing: expert groups (0 = off)
+    topk_groups: int = 0        # groups kept per token
 
     def replace(self, **kw) -> "MoEShape":
         return dataclasses.replace(self, **kw)

@@ -25,7 +25,7 @@ def layer_spec(shape) -> O.LayerSpec:
     return O.LayerSpec(shape.T, shape.d, shape.E, shape.k, shape.F, shape.n_shared,
                        shape.score, shape.renormalize, float(np.float32(shape.tau)),
                        shape.bias_mode, float(np.float32(shape.capacity_factor)),
-                       shape.reroute_depth)
+                       shape.reroute_depth, shape.n_groups, shape.topk_groups)
 
 
 def expert_weights(inp, experts=None) -> O.ExpertWeights:

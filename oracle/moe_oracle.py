@@ -92,6 +92,8 @@ class RouteConfig:
     renormalize: int = 1
     tau: float = 1.0
     bias_mode: int = BIAS_NONE
+    n_groups: int = 0        # group-limited routing: experts in n_groups blocks (0/1 = off)
+    topk_groups: int = 0     # groups kept per token
 
 
 def selection_keys(z: np.ndarray, rc: RouteConfig, bias=None, u=None):
@@ -190,10 +192,42 @@ class Routing:
     fallback: Optional[np.ndarray] = None  # [T,depth] int32 next-best experts, or None
 
 
+def group_limited_keys(keys: np.ndarray, n_groups: int, topk_groups: int):
+    """Two-level routing ([P3] closing case: experts clustered into groups, a
+    router first decides the group, then the original router picks the experts
+    inside it).  Reading: the experts form n_groups contiguous blocks of E /
+    n_groups; a group's score is its largest key (the group holding the token's
+    best expert comes first); the topk_groups best groups are kept, ties to the
+    lower group; the other experts' keys become -inf so the top-k cannot take
+    them.  Returns (limited keys float32, gap between the last kept and the first
+    dropped group score, float64)."""
+    keys = np.asarray(keys, np.float32)
+    T, E = keys.shape
+    gsz = E // n_groups
+    gscore = keys.reshape(T, n_groups, gsz).max(axis=2).astype(np.float64)
+    order = np.argsort(-gscore, axis=1, kind="stable")
+    keep = np.zeros((T, n_groups), bool)
+    np.put_along_axis(keep, order[:, :topk_groups], True, axis=1)
+    srt = np.take_along_axis(gscore, order, axis=1)
+    gap = srt[:, topk_groups - 1] - srt[:, topk_groups] if topk_groups < n_groups else np.full(T, np.inf)
+    limited = np.where(np.repeat(keep, gsz, axis=1), keys, np.float32(-np.inf)).astype(np.float32)
+    return limited, gap
+
+
 def route_from_logits(z, rc: RouteConfig, bias=None, u=None, depth: int = 0) -> Routing:
     """S2 on given float32 logits: keys -> top-k -> gate weights (and the
-    `depth` fallback experts for overflow re-routing)."""
+    `depth` fallback experts for overflow re-routing).  With group-limited
+    routing the top-k runs over the kept groups' experts only (the weights are
+    formed as without it) and gap_sel also covers the group decision."""
     keys, basis = selection_keys(z, rc, bias, u)
+    if rc.n_groups > 1:
+        limited, ggap = group_limited_keys(keys, rc.n_groups, rc.topk_groups)
+        idx, gs, go = topk_by_keys(limited, rc.k)
+        gs = np.where(np.isfinite(gs), gs, np.inf)
+        gs = np.minimum(gs, ggap)
+        w = gate_weights(basis, idx, rc)
+        fb = fallback_candidates(limited, rc.k, depth) if depth else None
+        return Routing(idx, w, keys, gs, go, fb)
     idx, gs, go = topk_by_keys(keys, rc.k)
     w = gate_weights(basis, idx, rc)
     fb = fallback_candidates(keys, rc.k, depth) if depth else None
@@ -504,10 +538,13 @@ class LayerSpec:
     bias_mode: int = BIAS_NONE
     capacity_factor: float = 0.0
     reroute_depth: int = 0
+    n_groups: int = 0
+    topk_groups: int = 0
 
     @property
     def route(self) -> RouteConfig:
-        return RouteConfig(self.E, self.k, self.score, self.renormalize, self.tau, self.bias_mode)
+        return RouteConfig(self.E, self.k, self.score, self.renormalize, self.tau, self.bias_mode,
+                           self.n_groups, self.topk_groups)
 
     @property
     def C(self) -> Optional[int]:

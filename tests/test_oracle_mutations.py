@@ -15,7 +15,8 @@ import tests.test_oracle_pins as pins
 _orig = {name: getattr(O, name) for name in
          ["router_logits", "gumbel_noise", "topk_by_keys", "gate_weights", "capacity",
           "permute", "swiglu_ffn", "combine", "fp8_e4m3fn_decode", "selection_keys",
-          "silu", "router_probs", "router_stats", "bias_update", "permute_reroute"]}
+          "silu", "router_probs", "router_stats", "bias_update", "permute_reroute",
+          "group_limited_keys"]}
 
 
 def m_router_wrong_column(x, w):
@@ -176,6 +177,28 @@ def m_reroute_rows_before_first_pass(idx, fb, E, C):
     return _reroute_variant(idx, fb, E, C, reroute_first=True)
 
 
+def m_group_score_sum(keys, n_groups, topk_groups):
+    keys = np.asarray(keys, np.float32)
+    T, E = keys.shape
+    gsz = E // n_groups
+    gscore = keys.reshape(T, n_groups, gsz).astype(np.float64).sum(axis=2)
+    order = np.argsort(-gscore, axis=1, kind="stable")
+    keep = np.zeros((T, n_groups), bool)
+    np.put_along_axis(keep, order[:, :topk_groups], True, axis=1)
+    return np.where(np.repeat(keep, gsz, axis=1), keys, np.float32(-np.inf)).astype(np.float32), \
+        np.full(T, np.inf)
+
+
+def m_group_interleaved(keys, n_groups, topk_groups):
+    keys = np.asarray(keys, np.float32)
+    T, E = keys.shape
+    perm = np.arange(E).reshape(E // n_groups, n_groups).T.ravel()  # group g = experts e with e % G == g
+    lim, gap = _orig["group_limited_keys"](keys[:, perm], n_groups, topk_groups)
+    out = np.empty_like(lim)
+    out[:, perm] = lim
+    return out, gap
+
+
 MUTATIONS = [
     ("router_logits", m_router_wrong_column, ["test_router_unit_vectors_select_rows"]),
     ("gumbel_noise", m_gumbel_sign, ["test_gumbel_statistics_match_gumbel01",
@@ -203,6 +226,8 @@ MUTATIONS = [
     ("permute_reroute", m_reroute_last_token_first, ["test_reroute_priority_goes_to_the_earlier_token",
                                                      "test_reroute_matches_deferred_acceptance_bruteforce"]),
     ("permute_reroute", m_reroute_rows_before_first_pass, ["test_reroute_rows_follow_the_first_pass"]),
+    ("group_limited_keys", m_group_score_sum, ["test_group_limit_hand_example", "test_group_limit_bruteforce"]),
+    ("group_limited_keys", m_group_interleaved, ["test_group_limit_hand_example"]),
 ]
 
 

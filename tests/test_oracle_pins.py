@@ -681,3 +681,47 @@ def test_rerouted_layer_serves_each_slot_by_its_fallback_expert():
     toks = list(range(T))
     got = O.token_outputs(toks, x, res.perm.dest_row, serving, res.routing.w, ew)
     np.testing.assert_allclose(got, res.out, rtol=1e-12, atol=1e-12)
+
+
+# -------------------------------------------------- group-limited routing
+def test_group_limit_hand_example():
+    """Keys (5, 1, 4, 3), groups {0,1} {2,3}, one group, top-2: group scores are
+    (5, 4), so group 0 is kept and the experts are (0, 1) -- not (0, 2) as
+    without groups.  Keeping both groups is plain top-k."""
+    keys = np.array([[5.0, 1.0, 4.0, 3.0]], np.float32)
+    r = O.route_from_logits(keys, O.RouteConfig(4, 2, n_groups=2, topk_groups=1))
+    np.testing.assert_array_equal(r.idx, [[0, 1]])
+    r2 = O.route_from_logits(keys, O.RouteConfig(4, 2, n_groups=2, topk_groups=2))
+    np.testing.assert_array_equal(r2.idx, [[0, 2]])
+    assert r.gap_sel[0] == 1.0  # the group decision: 5 against 4
+
+
+def test_group_limit_bruteforce():
+    """Random keys: the chosen experts are the top-k of the union of the M groups
+    with the largest maxima (brute force over every M-subset of groups), and the
+    token's best expert is always among them."""
+    r = _rng(31)
+    for trial in range(200):
+        G = int(r.choice([2, 4, 8]))
+        gs = int(r.choice([2, 3, 4]))
+        E = G * gs
+        M = int(r.integers(1, G + 1))
+        k = int(r.integers(1, M * gs + 1))
+        keys = r.standard_normal((1, E)).astype(np.float32)
+        got = O.route_from_logits(keys, O.RouteConfig(E, k, n_groups=G, topk_groups=M)).idx[0]
+        gmax = keys[0].reshape(G, gs).max(axis=1)
+        best = max(itertools.combinations(range(G), M), key=lambda c: sorted(gmax[list(c)], reverse=True))
+        allowed = [e for g in best for e in range(g * gs, (g + 1) * gs)]
+        want = sorted(allowed, key=lambda e: -keys[0, e])[:k]
+        assert list(got) == want, trial
+        assert int(np.argmax(keys[0])) in got
+
+
+def test_group_limit_off_is_plain_routing():
+    r = _rng(32)
+    z = r.standard_normal((30, 16)).astype(np.float32)
+    for G in (0, 1):
+        a = O.route_from_logits(z, O.RouteConfig(16, 3, n_groups=G, topk_groups=1))
+        b = O.route_from_logits(z, O.RouteConfig(16, 3))
+        np.testing.assert_array_equal(a.idx, b.idx)
+        np.testing.assert_array_equal(a.w, b.w)
