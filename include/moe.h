@@ -100,6 +100,13 @@ typedef struct {
   int32_t reroute_depth;     /* overflow re-routing ([P2] s3.2 level 2): 0 = off, else D  */
                              /* in 1 .. min(8, E - top_k) fallback experts per token;      */
                              /* needs top_k <= 64; acts only under a capacity limit        */
+  int32_t n_groups;          /* group-limited routing ([P3] closing case: the group first, */
+                             /* then the router inside it): 0 or 1 = off; else the experts */
+                             /* form n_groups contiguous blocks (n_groups divides E)       */
+  int32_t topk_groups;       /* groups kept per token: the ones with the largest maximum   */
+                             /* key, ties to the lower group; the top-k (and fallbacks)    */
+                             /* come from their experts: top_k + reroute_depth <=          */
+                             /* topk_groups * E / n_groups                                 */
 } moe_config;
 
 /* Expert weights.  Scales are required for fp8 and must be NULL otherwise.

@@ -39,7 +39,8 @@ class moe_config(ctypes.Structure):
                 ("score", ctypes.c_int32), ("renormalize", ctypes.c_int32), ("tau", ctypes.c_float),
                 ("bias_mode", ctypes.c_int32), ("capacity_factor", ctypes.c_float),
                 ("act_dtype", ctypes.c_int32), ("w_dtype", ctypes.c_int32),
-                ("out_dtype", ctypes.c_int32), ("reroute_depth", ctypes.c_int32)]
+                ("out_dtype", ctypes.c_int32), ("reroute_depth", ctypes.c_int32),
+                ("n_groups", ctypes.c_int32), ("topk_groups", ctypes.c_int32)]
 
 
 class moe_expert_weights(ctypes.Structure):
@@ -121,7 +122,8 @@ def make_config(shape: W.MoEShape, out_dtype: Optional[int] = None) -> moe_confi
     return moe_config(shape.T, shape.d, shape.E, shape.k, shape.F, shape.n_shared, shape.score,
                       shape.renormalize, shape.tau, shape.bias_mode, shape.capacity_factor,
                       shape.act_dtype, shape.w_dtype,
-                      shape.out_dtype if out_dtype is None else out_dtype, shape.reroute_depth)
+                      shape.out_dtype if out_dtype is None else out_dtype, shape.reroute_depth,
+                      shape.n_groups, shape.topk_groups)
 
 
 def workspace_bytes(cfg: moe_config) -> int:

@@ -80,6 +80,7 @@ struct RouteLaunch {
   float tau;
   // bf16 path: padded expert count, d-split, and workspace buffers
   int fb = 0;               // fallback experts written after the top-k (topk_idx has k + fb columns)
+  int n_groups = 0, topk_groups = 0;  // group-limited routing (0 = off)
   int ep = 0, split = 0;
   uint16_t* wt = nullptr;   // [3][ep][d] split router weights
   float* part = nullptr;    // [split][T][ep] logit partials

@@ -125,11 +125,19 @@ moe_status check_config(const moe_config* c) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "reroute_depth = %d outside [0, min(8, E - top_k)]", c->reroute_depth);
   if (c->reroute_depth > 0 && c->top_k > 64)
     return fail(MOE_ERR_UNSUPPORTED, "overflow re-routing needs top_k <= 64");
+  if (c->n_groups < 0 || c->n_groups > c->E || (c->n_groups > 1 && c->E % c->n_groups))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "n_groups = %d must divide E = %d", c->n_groups, c->E);
+  if (c->n_groups > 1) {
+    if (c->topk_groups < 1 || c->topk_groups > c->n_groups)
+      return fail(MOE_ERR_INVALID_ARGUMENT, "topk_groups = %d outside [1, n_groups]", c->topk_groups);
+    if (c->top_k + c->reroute_depth > c->topk_groups * (c->E / c->n_groups))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "top_k + reroute_depth exceeds the experts of the kept groups");
+  }
   return MOE_OK;
 }
 
 // C = max(1, floor(T*k/E*cf)) in double from the float32 factor; -1 = no limit.
-static_assert(sizeof(moe_config) == 15 * 4, "moe_config layout is part of the ABI");
+static_assert(sizeof(moe_config) == 17 * 4, "moe_config layout is part of the ABI");
 static_assert(sizeof(moe_expert_weights) == 12 * 8, "moe_expert_weights layout is part of the ABI");
 
 int64_t capacity_of(const moe_config* c) {
@@ -258,6 +266,8 @@ moe_status run_route(const moe_config* c, const void* x, const float* w_router, 
                 c->score, c->renormalize, c->bias_mode, c->act_dtype, c->tau};
   const Layout L = layout_of(c);
   r.fb = c->reroute_depth;
+  r.n_groups = c->n_groups > 1 ? c->n_groups : 0;
+  r.topk_groups = c->topk_groups;
   r.ep = L.route_ep;
   r.split = L.route_split;
   r.wt = (uint16_t*)(ws + L.route_wt);

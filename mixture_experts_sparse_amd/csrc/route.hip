@@ -105,6 +105,37 @@ __device__ __forceinline__ void route_token(const RouteLaunch& a, int t, int lan
   float sel_b[4];
 #pragma unroll
   for (int s = 0; s < 4; ++s) { sel_e[s] = 0; sel_b[s] = 0.f; }
+  // group-limited routing: topk_groups rounds of the same arg-max pick the
+  // groups (a group's score is its largest key, so the best remaining expert
+  // names the best remaining group); every expert outside them is then taken
+  if (a.n_groups > 1) {
+    const int gsz = E / a.n_groups;
+    bool gone[EPL], kept[EPL];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      gone[i] = taken[i];
+      kept[i] = false;
+    }
+    for (int g = 0; g < a.topk_groups; ++g) {
+      Cand c{-FLT_MAX, 0.f, INT32_MAX};
+#pragma unroll
+      for (int i = 0; i < EPL; ++i) {
+        Cand o{key[i], basis[i], gone[i] ? INT32_MAX : lane + 64 * i};
+        if (better(o, c)) c = o;
+      }
+      c = wave_argmax(c);
+      const int grp = c.e / gsz;
+#pragma unroll
+      for (int i = 0; i < EPL; ++i)
+        if (!taken[i] && (lane + 64 * i) / gsz == grp) {
+          gone[i] = true;
+          kept[i] = true;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) taken[i] = taken[i] || !kept[i];
+  }
+
   // k + fb rounds: the top-k, then the fallback experts for overflow re-routing
   for (int j = 0; j < a.k + a.fb; ++j) {
     Cand c{-FLT_MAX, 0.f, INT32_MAX};

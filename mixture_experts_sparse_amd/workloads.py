@@ -89,6 +89,10 @@ WORKLOADS: Dict[str, MoEShape] = {
     "skewed_fp8": MoEShape("skewed_fp8", T=16384, d=4096, E=128, k=2, F=1536,
                            bias_mode=BIAS_LOGIT, bias_kind="zipf1.2",
                            capacity_factor=1.25, w_dtype=DT_FP8, seed=1238),
+    # the fine-grained layer with group-limited routing: 8 groups of 32, 4 kept
+    "fine_grouped_bf16": MoEShape("fine_grouped_bf16", T=8192, d=7168, E=256, k=8, F=2048, n_shared=1,
+                                  score=SCORE_SIGMOID, bias_mode=BIAS_SELECT_ONLY, bias_kind="normal0.5",
+                                  seed=1237, n_groups=8, topk_groups=4),
     # the skewed layer with overflow re-routing to the four next-best experts
     "skewed_fp8_reroute": MoEShape("skewed_fp8_reroute", T=16384, d=4096, E=128, k=2, F=1536,
                                    bias_mode=BIAS_LOGIT, bias_kind="zipf1.2", capacity_factor=1.25,

@@ -140,7 +140,10 @@ def check_routing(inp: W.MoEInputs, g: dict, report: dict):
     g_idx = g["topk_idx"][:, : sh.k]
     if D:
         # fallback experts, in order, away from near-ties among the first k + D + 1 keys
-        srt = -np.sort(-r.keys.astype(np.float64), axis=1)[:, : min(sh.k + D + 1, sh.E)]
+        keys = r.keys
+        if spec.route.n_groups > 1:
+            keys, _ = O.group_limited_keys(keys, spec.route.n_groups, spec.route.topk_groups)
+        srt = -np.sort(-keys.astype(np.float64), axis=1)[:, : min(sh.k + D + 1, sh.E)]
         fb_tie = np.min(srt[:, :-1] - srt[:, 1:], axis=1) < NEAR_TIE
         report["near_tie_fallback"] = int(fb_tie.sum())
         assert np.array_equal(g["topk_idx"][~fb_tie, sh.k:], r.fallback[~fb_tie]), "fallback experts differ"

@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_struct_layout_matches_header(L):
-    assert ctypes.sizeof(L.moe_config) == 15 * 4  # static_assert'ed in moe_api.hip too
+    assert ctypes.sizeof(L.moe_config) == 17 * 4  # static_assert'ed in moe_api.hip too
     assert ctypes.sizeof(L.moe_expert_weights) == 12 * 8
     assert ctypes.sizeof(L.moe_routing_out) == 4 * 8
     assert ctypes.sizeof(L.moe_kernel_time) == 64
@@ -69,6 +69,8 @@ def _cfg(L, **kw):
     (dict(capacity_factor=float("inf")), 1), (dict(renormalize=3), 1),
     (dict(reroute_depth=-1), 1), (dict(reroute_depth=9, E=64), 1), (dict(reroute_depth=7), 1),
     (dict(reroute_depth=1, E=128, k=65), 2),
+    (dict(n_groups=3), 1), (dict(n_groups=4, topk_groups=0), 1), (dict(n_groups=4, topk_groups=5), 1),
+    (dict(n_groups=4, topk_groups=1, k=3), 1), (dict(n_groups=4, topk_groups=1, reroute_depth=1), 1),
 ])
 def test_invalid_configs_rejected(L, kw, status):
     cfg = _cfg(L, **kw)

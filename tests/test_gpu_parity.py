@@ -42,6 +42,16 @@ SMALL = {
                                              capacity_factor=1.0, reroute_depth=2),
     "reroute_decode": WK["skewed_fp8_decode"].replace(reroute_depth=8),
     "reroute_f32": WK["tiny_fp32"].replace(name="rrf", capacity_factor=0.75, reroute_depth=2),
+    # group-limited routing: 256 experts in 8 groups, 4 kept, top-8 (sigmoid, shared
+    # expert); one group of 16 kept, top-2 (the skewed fp8 router); groups with
+    # overflow re-routing inside the kept groups
+    "grouped_fine": W.shrink(WK["fine_shared_bf16"], T=150, d=256, F=128).replace(n_groups=8, topk_groups=4),
+    "grouped_one": W.shrink(WK["skewed_fp8"], T=300, d=256, F=256).replace(n_groups=8, topk_groups=1),
+    # (no bias: at this small d a bias would send most tokens to a few experts and
+    # drop nearly everything; here 66 of 800 pairs are re-routed, 13 tokens lose all)
+    "grouped_reroute": WK["mixtral_bf16"].replace(name="grr", T=400, d=128, E=64, k=2, F=128,
+                                                  capacity_factor=1.0, reroute_depth=3,
+                                                  n_groups=8, topk_groups=2),
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
