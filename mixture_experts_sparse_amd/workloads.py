@@ -29,7 +29,7 @@ import torch
 # enums mirrored from include/moe.h (kept as plain ints)
 SCORE_SOFTMAX, SCORE_SIGMOID = 0, 1
 BIAS_NONE, BIAS_LOGIT, BIAS_SELECT_ONLY = 0, 1, 2
-DT_F32, DT_BF16, DT_FP8 = 0, 1, 2
+DT_F32, DT_BF16, DT_FP8, DT_INT4 = 0, 1, 2, 3
 
 FP8_E4M3FN_MAX = 448.0
 
@@ -101,6 +101,11 @@ WORKLOADS: Dict[str, MoEShape] = {
     "skewed_fp8_decode": MoEShape("skewed_fp8_decode", T=32, d=4096, E=128, k=2,
                                   F=1536, bias_mode=BIAS_LOGIT, bias_kind="zipf1.2",
                                   capacity_factor=1.25, w_dtype=DT_FP8, seed=1238),
+    # decode size with group-wise INT4 expert weights (128 per group, fp16 scale
+    # and 4-bit zero point per group), bf16 activations, fp32 router
+    "skewed_int4_decode": MoEShape("skewed_int4_decode", T=32, d=4096, E=128, k=2,
+                                   F=1536, bias_mode=BIAS_LOGIT, bias_kind="zipf1.2",
+                                   capacity_factor=1.25, w_dtype=DT_INT4, seed=1238),
 }
 
 # Zipf exponent of the skewed workload, and the logit-scale lambda that turns
@@ -143,6 +148,29 @@ def quantize_rows_fp8(w: torch.Tensor):
     return q.view(torch.uint8), scale.squeeze(-1).contiguous()
 
 
+INT4_GROUP = 128
+
+
+def quantize_groups_int4(w: torch.Tensor):
+    """Group-wise asymmetric INT4 quantisation of a float32 [..., rows, cols]
+    tensor, 128 consecutive columns per group: scale = (max - min) / 15 (1 when
+    the group is constant), zero = clamp(RNE(-min / scale), 0, 15), code =
+    clamp(RNE(w / scale) + zero, 0, 15).  Returns (codes packed two per byte, the
+    even column in the low nibble, uint8 [..., rows, cols/2]; group parameters
+    [..., rows, cols/128], each the 32-bit word fp16 scale bits | zero << 16,
+    held in an int32 tensor).  This is how the INT4
+    workload's *inputs* are made; the layer itself only ever decodes them."""
+    g = w.reshape(*w.shape[:-1], w.shape[-1] // INT4_GROUP, INT4_GROUP)
+    lo, hi = g.amin(dim=-1, keepdim=True), g.amax(dim=-1, keepdim=True)
+    scale = torch.where(hi > lo, (hi - lo) / 15.0, torch.ones_like(hi))
+    zero = torch.round(-lo / scale).clamp_(0, 15)
+    q = (torch.round(g / scale) + zero).clamp_(0, 15).to(torch.uint8).reshape(w.shape)
+    packed = (q[..., 0::2] | (q[..., 1::2] << 4)).contiguous()
+    s16 = scale.squeeze(-1).to(torch.float16).view(torch.int16).to(torch.int64) & 0xFFFF
+    qp = (s16 | (zero.squeeze(-1).to(torch.int64) << 16)).to(torch.int32).contiguous()
+    return packed, qp
+
+
 def _store_weight(w32: torch.Tensor, w_dtype: int):
     if w_dtype == DT_F32:
         return w32, None
@@ -150,6 +178,8 @@ def _store_weight(w32: torch.Tensor, w_dtype: int):
         return w32.to(torch.bfloat16), None
     if w_dtype == DT_FP8:
         return quantize_rows_fp8(w32)
+    if w_dtype == DT_INT4:
+        return quantize_groups_int4(w32)
     raise ValueError(w_dtype)
 
 
@@ -162,9 +192,13 @@ def _expert_tensor(shape: MoEShape, name: str, n_exp: int, rows: int, cols: int,
         dt = torch.bfloat16
     else:
         dt = torch.uint8
-    out = torch.empty((n_exp, rows, cols), dtype=dt, device=device)
-    scales = (torch.empty((n_exp, rows), dtype=torch.float32, device=device)
-              if w_dtype == DT_FP8 else None)
+    out = torch.empty((n_exp, rows, cols // 2 if w_dtype == DT_INT4 else cols), dtype=dt, device=device)
+    if w_dtype == DT_FP8:
+        scales = torch.empty((n_exp, rows), dtype=torch.float32, device=device)
+    elif w_dtype == DT_INT4:
+        scales = torch.empty((n_exp, rows, cols // INT4_GROUP), dtype=torch.int32, device=device)
+    else:
+        scales = None
     for e in range(n_exp):
         w32 = _normal((rows, cols), 0.02, child_seed(shape.seed, name, e), device)
         w, s = _store_weight(w32, w_dtype)
@@ -279,5 +313,5 @@ def shrink(shape: MoEShape, T: int, d: int, F: int, name: Optional[str] = None) 
 
 
 def nbytes_of(dtype: int) -> int:
-    return {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[dtype]
+    return {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[dtype]  # (INT4: half a byte, plus group parameters)
 

@@ -20,6 +20,13 @@ def to_np(t):
     return t.cpu().numpy()
 
 
+def scales_np(t):
+    """Weight scales: float32 row scales (fp8) as they are; INT4 group words,
+    held in int32 tensors, reinterpreted as the uint32 words they are."""
+    a = to_np(t)
+    return a.view(np.uint32) if a is not None and a.dtype == np.int32 else a
+
+
 def layer_spec(shape) -> O.LayerSpec:
     """The layer as the C ABI receives it: tau and the capacity factor are float32 there."""
     return O.LayerSpec(shape.T, shape.d, shape.E, shape.k, shape.F, shape.n_shared,
@@ -32,7 +39,7 @@ def expert_weights(inp, experts=None) -> O.ExpertWeights:
     """Host copies of the routed experts (all, or only ``experts`` -- others left zero-sized)."""
     if experts is None:
         return O.ExpertWeights(to_np(inp.w_gate), to_np(inp.w_up), to_np(inp.w_down),
-                               to_np(inp.s_gate), to_np(inp.s_up), to_np(inp.s_down))
+                               scales_np(inp.s_gate), scales_np(inp.s_up), scales_np(inp.s_down))
     return _LazyExperts(inp)
 
 
@@ -45,9 +52,9 @@ class _LazyExperts(O.ExpertWeights):
 
     def expert(self, e: int):
         i = self._inp
-        sg = None if i.s_gate is None else to_np(i.s_gate[e])
-        su = None if i.s_up is None else to_np(i.s_up[e])
-        sd = None if i.s_down is None else to_np(i.s_down[e])
+        sg = None if i.s_gate is None else scales_np(i.s_gate[e])
+        su = None if i.s_up is None else scales_np(i.s_up[e])
+        sd = None if i.s_down is None else scales_np(i.s_down[e])
         return (O.dequant(to_np(i.w_gate[e]), sg), O.dequant(to_np(i.w_up[e]), su),
                 O.dequant(to_np(i.w_down[e]), sd))
 
@@ -56,7 +63,7 @@ def shared_weights(inp):
     if inp.sh_gate is None:
         return None
     return O.ExpertWeights(to_np(inp.sh_gate), to_np(inp.sh_up), to_np(inp.sh_down),
-                           to_np(inp.sh_s_gate), to_np(inp.sh_s_up), to_np(inp.sh_s_down))
+                           scales_np(inp.sh_s_gate), scales_np(inp.sh_s_up), scales_np(inp.sh_s_down))
 
 
 def forward(inp) -> O.LayerResult:

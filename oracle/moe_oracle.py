@@ -440,9 +440,37 @@ def fp8_e4m3fn_decode(codes: np.ndarray) -> np.ndarray:
     return np.where(s == 1, -mag, mag)
 
 
+INT4_GROUP = 128
+
+
+def int4_dequant(packed, qparams) -> np.ndarray:
+    """Group-wise INT4 expert weights to float64.
+
+    [P3] s4.2 (quantisation and mixed precision): expert weights can be kept in
+    INT4 while the router stays in higher precision, quantised group-wise --
+    every 128 weights a group with its own scale and zero point.  Reading of the
+    layout (the page gives none): groups run along each output row's input
+    dimension; codes q in 0..15, two per byte, k = 2b in the low nibble of byte
+    b and k = 2b + 1 in the high nibble ([..., N, K/2] uint8); per group one
+    uint32, bits 0..15 the scale as IEEE fp16 and bits 16..19 the zero point z
+    ([..., N, K/128]).  w[n, k] = scale * (q - z).
+    """
+    p = np.asarray(packed, dtype=np.uint8)
+    q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.int64)
+    q[..., 0::2] = p & 0xF
+    q[..., 1::2] = p >> 4
+    qp = np.asarray(qparams, dtype=np.uint32)
+    scale = (qp & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    zero = ((qp >> 16) & 0xF).astype(np.int64)
+    return np.repeat(scale, INT4_GROUP, axis=-1) * (q - np.repeat(zero, INT4_GROUP, axis=-1))
+
+
 def dequant(w, scale=None) -> np.ndarray:
-    """Expert weight matrix to float64: widen f32/bf16, or fp8 code * row scale."""
+    """Expert weight matrix to float64: widen f32/bf16, fp8 code * row scale, or
+    group-wise INT4 (uint32 group parameters)."""
     w = np.asarray(w)
+    if scale is not None and np.asarray(scale).dtype == np.uint32:
+        return int4_dequant(w, scale)
     if w.dtype == np.uint8:
         return fp8_e4m3fn_decode(w) * np.asarray(scale, dtype=np.float64)[..., :, None]
     return w.astype(np.float64)

@@ -16,7 +16,7 @@ _orig = {name: getattr(O, name) for name in
          ["router_logits", "gumbel_noise", "topk_by_keys", "gate_weights", "capacity",
           "permute", "swiglu_ffn", "combine", "fp8_e4m3fn_decode", "selection_keys",
           "silu", "router_probs", "router_stats", "bias_update", "permute_reroute",
-          "group_limited_keys"]}
+          "group_limited_keys", "int4_dequant"]}
 
 
 def m_router_wrong_column(x, w):
@@ -199,6 +199,31 @@ def m_group_interleaved(keys, n_groups, topk_groups):
     return out, gap
 
 
+def m_int4_nibbles_swapped(packed, qp):
+    p = np.asarray(packed, np.uint8)
+    return _orig["int4_dequant"]((p >> 4) | ((p & 15) << 4), qp)
+
+
+def m_int4_zero_ignored(packed, qp):
+    return _orig["int4_dequant"](packed, np.asarray(qp, np.uint32) & 0xFFFF)
+
+
+def m_int4_groups_interleaved(packed, qp):
+    """Group g of a row taken as columns g, g + G, g + 2G, ... instead of a block."""
+    p = np.asarray(packed, np.uint8)
+    q = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.int64)
+    q[..., 0::2], q[..., 1::2] = p & 15, p >> 4
+    qp = np.asarray(qp, np.uint32)
+    s = (qp & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64)
+    z = ((qp >> 16) & 15).astype(np.int64)
+    reps = q.shape[-1] // qp.shape[-1]
+    return np.tile(s, reps) * (q - np.tile(z, reps))
+
+
+def m_int4_sign_flipped(packed, qp):
+    return -_orig["int4_dequant"](packed, qp)
+
+
 MUTATIONS = [
     ("router_logits", m_router_wrong_column, ["test_router_unit_vectors_select_rows"]),
     ("gumbel_noise", m_gumbel_sign, ["test_gumbel_statistics_match_gumbel01",
@@ -228,6 +253,11 @@ MUTATIONS = [
     ("permute_reroute", m_reroute_rows_before_first_pass, ["test_reroute_rows_follow_the_first_pass"]),
     ("group_limited_keys", m_group_score_sum, ["test_group_limit_hand_example", "test_group_limit_bruteforce"]),
     ("group_limited_keys", m_group_interleaved, ["test_group_limit_hand_example"]),
+    ("int4_dequant", m_int4_nibbles_swapped, ["test_int4_hand_example", "test_int4_every_code_and_zero_point"]),
+    ("int4_dequant", m_int4_zero_ignored, ["test_int4_hand_example", "test_int4_every_code_and_zero_point",
+                                           "test_int4_groups_take_their_own_parameters"]),
+    ("int4_dequant", m_int4_groups_interleaved, ["test_int4_groups_take_their_own_parameters"]),
+    ("int4_dequant", m_int4_sign_flipped, ["test_int4_hand_example", "test_int4_every_code_and_zero_point"]),
 ]
 
 

@@ -306,6 +306,60 @@ def test_fp8_decode_all_codes():
     assert dec[0x80] == 0.0 and dec[0xFE] == -448.0
 
 
+# ---------------------------------------------------------------- INT4 groups
+def _qp(scale_bits, zero):
+    return np.uint32(scale_bits | (zero << 16))
+
+
+def test_int4_hand_example():
+    """[P3] s4.2 group-wise INT4: one 128-wide group, scale 0.5 (fp16 0x3800),
+    zero point 1.  Byte 0 = 0x21 holds codes 1 (k=0, low nibble) and 2 (k=1),
+    byte 1 = 0xF0 holds 0 and 15; the rest 0x11 (code 1, value 0)."""
+    row = np.full((1, 64), 0x11, np.uint8)
+    row[0, 0], row[0, 1] = 0x21, 0xF0
+    w = O.int4_dequant(row, np.array([[_qp(0x3800, 1)]], np.uint32))
+    assert w.shape == (1, 128)
+    np.testing.assert_array_equal(w[0, :4], [0.0, 0.5, -0.5, 7.0])
+    assert np.all(w[0, 4:] == 0.0)
+
+
+def test_int4_every_code_and_zero_point():
+    """Scale 1 (fp16 0x3C00): byte b decodes to (b & 15) - z at k = 2b and
+    (b >> 4) - z at k = 2b + 1, for all 256 bytes and all 16 zero points."""
+    packed = np.tile(np.arange(256, dtype=np.uint8), (16, 1))   # K = 512: four groups
+    qp = np.array([[_qp(0x3C00, z)] * 4 for z in range(16)], np.uint32)
+    w = O.int4_dequant(packed, qp)
+    b = np.arange(256)
+    for z in range(16):
+        assert np.array_equal(w[z, 0::2], (b & 15) - z)
+        assert np.array_equal(w[z, 1::2], (b >> 4) - z)
+
+
+def test_int4_groups_take_their_own_parameters():
+    """Two groups per row, two rows: columns 0..127 use the row's first word,
+    128..255 the second; fp16 scale bits decode by the IEEE formula
+    2^(e-15) (1 + m/1024) for normal numbers and m 2^-24 for subnormal ones."""
+    def f16(bits):
+        e, m = (bits >> 10) & 31, bits & 1023
+        v = m * 2.0 ** -24 if e == 0 else 2.0 ** (e - 15) * (1 + m / 1024)
+        return -v if bits & 0x8000 else v
+    packed = np.full((2, 128), 0x77, np.uint8)  # every code 7
+    bits = [[0x4000, 0x3555], [0x0003, 0x7BFF]]
+    zeros = [[3, 9], [0, 15]]
+    qp = np.array([[_qp(bits[r][g], zeros[r][g]) for g in range(2)] for r in range(2)], np.uint32)
+    w = O.int4_dequant(packed, qp)
+    for r in range(2):
+        for g in range(2):
+            assert np.all(w[r, 128 * g:128 * (g + 1)] == f16(bits[r][g]) * (7 - zeros[r][g])), (r, g)
+
+
+def test_int4_expert_dequant_dispatches_on_group_words():
+    """dequant() takes the INT4 path for uint32 group words, fp8 for float scales."""
+    packed = np.full((3, 64), 0x98, np.uint8)   # codes 8, 9
+    w = O.dequant(packed, np.full((3, 1), _qp(0x3C00, 8), np.uint32))
+    assert w.shape == (3, 128) and np.all(w[:, 0::2] == 0.0) and np.all(w[:, 1::2] == 1.0)
+
+
 # ---------------------------------------------------------------- S5/S6 experts
 def _dense_ffn_torch(x, wg, wu, wd):
     """SwiGLU from torch's library routines (linear, silu) in float64."""

@@ -28,6 +28,30 @@ def test_fp8_inputs_are_codes_with_row_scales():
     assert np.abs(dec).max() < 0.2
 
 
+def test_int4_inputs_are_groups_that_round_trip():
+    """INT4 inputs: packed codes [E, rows, cols/2], one word per 128 columns; the
+    oracle's decode of them is within half a step (plus the fp16 rounding of the
+    scale) of the float32 weights they were made from, and the extreme weights
+    of each group land on codes 0 and 15."""
+    sh = W.shrink(W.WORKLOADS["skewed_int4_decode"], T=8, d=256, F=384)
+    i = W.make_inputs(sh)
+    assert i.w_gate.dtype == torch.uint8 and i.w_gate.shape == (128, 384, 128)
+    assert i.s_gate.dtype == torch.int32 and i.s_gate.shape == (128, 384, 2)
+    assert i.w_down.shape == (128, 256, 192) and i.s_down.shape == (128, 256, 3)
+    w32 = W._normal((384, 256), 0.02, W.child_seed(sh.seed, "w_gate", 5), "cpu").double().numpy()
+    qp = i.s_gate[5].numpy().view(np.uint32)
+    dec = O.dequant(i.w_gate[5].numpy(), qp)
+    step = np.repeat((qp & 0xFFFF).astype(np.uint16).view(np.float16).astype(np.float64), 128, axis=1)
+    assert np.all(np.abs(dec - w32) <= 0.51 * step)
+    p = i.w_gate[5].numpy()
+    codes = np.empty((384, 256), np.int64)
+    codes[:, 0::2], codes[:, 1::2] = p & 15, p >> 4
+    g = w32.reshape(384, 2, 128)
+    cg = codes.reshape(384, 2, 128)
+    r, gi = np.meshgrid(np.arange(384), np.arange(2), indexing="ij")
+    assert np.all(cg[r, gi, g.argmin(-1)] == 0) and np.all(cg[r, gi, g.argmax(-1)] == 15)
+
+
 def test_gumbel_uniforms_are_open_interval_float32():
     u = W.gumbel_uniforms(W.WORKLOADS["gumbel_bf16"])
     assert u.dtype == np.float32 and u.shape == (2048, 16)
