@@ -93,7 +93,13 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
     wb = W.nbytes_of(sh.w_dtype)
     hb = 4 if sh.w_dtype == W.DT_F32 else 2
     T, d, E, k, F, N = sh.T, sh.d, sh.E, sh.k, sh.F, kept_rows
-    scale_b = 4 * (2 * F + d) if sh.w_dtype == W.DT_FP8 else 0
+    # scales: fp8 one f32 per weight row; INT4 one 32-bit word per 128 weights of a row
+    if sh.w_dtype == W.DT_FP8:
+        sc_gu, sc_dn = 4 * 2 * F, 4 * d
+    elif sh.w_dtype == W.DT_INT4:
+        sc_gu, sc_dn = 4 * 2 * F * (d // 128), 4 * d * (F // 128)
+    else:
+        sc_gu = sc_dn = 0
     ep = 16
     while ep < E:
         ep *= 2
@@ -111,9 +117,9 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
         "gemm_tiles": {"bytes": 0},
         # gate/up: x_perm read, both weight matrices of every touched expert, h written
         "gemm_gate_up": {"flop": 4.0 * N * d * F,
-                         "bytes": N * d * a + touched * (2 * F * d * wb) + touched * scale_b + N * F * hb},
+                         "bytes": N * d * a + touched * (2 * F * d * wb + sc_gu) + N * F * hb},
         "gemm_down": {"flop": 2.0 * N * F * d,
-                      "bytes": N * F * hb + touched * (d * F * wb) + N * d * 4},
+                      "bytes": N * F * hb + touched * (d * F * wb + sc_dn) + N * d * 4},
         # kept rows of y (f32) read once, output written once (+ shared rows)
         "combine": {"bytes": N * d * 4 + T * d * (4 if sh.out_dtype == W.DT_F32 else 2)
                     + T * k * 8 + (T * d * 4 if sh.n_shared else 0)},
@@ -121,15 +127,16 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
     # load balancing (--balance): the logits (and Gumbel uniforms) read once
     work["balance_stats"] = {"bytes": T * E * 4 * (2 if sh.gumbel else 1)}
     if sh.n_shared:
-        work["shared_gate_up"] = {"flop": 4.0 * T * d * F, "bytes": T * d * a + 2 * F * d * wb + T * F * hb}
-        work["shared_down"] = {"flop": 2.0 * T * F * d, "bytes": T * F * hb + d * F * wb + T * d * 4}
+        work["shared_gate_up"] = {"flop": 4.0 * T * d * F, "bytes": T * d * a + 2 * F * d * wb + sc_gu + T * F * hb}
+        work["shared_down"] = {"flop": 2.0 * T * F * d, "bytes": T * F * hb + d * F * wb + sc_dn + T * d * 4}
     return work
 
 
 def kernel_key(name: str) -> str:
     """Library kernel name -> work key (drops the dtype tags)."""
-    n = name.replace("_f32", "").replace("_bf16", "").replace("_fp8", "")
-    return n
+    for tag in ("_f32", "_bf16", "_fp8", "_int4"):
+        name = name.replace(tag, "")
+    return name
 
 
 def cpu_baseline(inp, sample: int):
@@ -233,8 +240,9 @@ def main():
     kept = int(st[sh.E:2 * sh.E].sum())
     touched = int((st[sh.E:2 * sh.E] > 0).sum())
     work = algorithmic_work(sh, kept, touched)
-    dt_name = {W.DT_BF16: "bf16", W.DT_FP8: "fp8", W.DT_F32: "f32"}[sh.w_dtype]
-    mfma_peak = PEAK_TFLOPS["bf16" if sh.w_dtype == W.DT_FP8 else dt_name]
+    dt_name = {W.DT_BF16: "bf16", W.DT_FP8: "fp8", W.DT_F32: "f32", W.DT_INT4: "int4"}[sh.w_dtype]
+    # fp8 and INT4 weights are decoded to bf16 and multiplied on the bf16 MFMA
+    mfma_peak = PEAK_TFLOPS["bf16" if sh.w_dtype in (W.DT_FP8, W.DT_INT4) else dt_name]
 
     kernels = {}
     for name, (launches, total_ms) in prof.items():

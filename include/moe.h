@@ -71,7 +71,10 @@ typedef enum {
   MOE_ERR_HIP = 4                /* a HIP launch or runtime call failed           */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3FN = 2 } moe_dtype;
+/* MOE_INT4 (expert weights only): group-wise 4-bit weights ([P3] s4.2
+ * quantisation: every 128 weights along a row's input dimension form a group
+ * with its own scale and zero point; w = scale * (q - zero)). */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_FP8_E4M3FN = 2, MOE_INT4 = 3 } moe_dtype;
 typedef enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 } moe_score;
 typedef enum {
   MOE_BIAS_NONE = 0,
@@ -95,7 +98,8 @@ typedef struct {
   float capacity_factor;     /* <= 0: no limit; else C = max(1, floor(T*k/E*cf))          */
   int32_t act_dtype;         /* x: MOE_F32 or MOE_BF16                                    */
   int32_t w_dtype;           /* expert weights: MOE_F32 (requires act F32), MOE_BF16,     */
-                             /* MOE_FP8_E4M3FN (requires act BF16)                        */
+                             /* MOE_FP8_E4M3FN (requires act BF16), MOE_INT4 (requires    */
+                             /* act BF16, F % 128 == 0 and d % 256 == 0)                  */
   int32_t out_dtype;         /* layer output: MOE_F32 or MOE_BF16                         */
   int32_t reroute_depth;     /* overflow re-routing ([P2] s3.2 level 2): 0 = off, else D  */
                              /* in 1 .. min(8, E - top_k) fallback experts per token;      */
@@ -109,14 +113,22 @@ typedef struct {
                              /* topk_groups * E / n_groups                                 */
 } moe_config;
 
-/* Expert weights.  Scales are required for fp8 and must be NULL otherwise.
- * The sh_* members describe the shared expert ([1,F,d], [1,F,d], [1,d,F]) and
- * must be non-NULL exactly when n_shared == 1. */
+/* Expert weights, row-major per expert: w_gate, w_up [E,F,d], w_down [E,d,F]
+ * (a row holds one output's weights over the input dimension), 16-byte aligned.
+ *   MOE_F32 / MOE_BF16: one element per weight; the s_* members NULL.
+ *   MOE_FP8_E4M3FN: one OCP e4m3fn code byte per weight; s_* = f32 scale per
+ *     row ([E,F] for gate/up, [E,d] for down), w = scale * decode(code).
+ *   MOE_INT4: two codes per byte, [E,F,d/2] and [E,d,F/2], the even input index
+ *     in the low nibble; s_* = one uint32 word per 128-weight group of a row
+ *     ([E,F,d/128], [E,d,F/128]; 4-byte aligned): bits 0..15 the fp16 scale,
+ *     bits 16..19 the zero point z, the rest ignored; w = scale * (q - z).
+ * The sh_* members describe the shared expert (E = 1 in the shapes above, same
+ * dtype) and must be non-NULL exactly when n_shared == 1. */
 typedef struct {
   const void* w_gate;  const void* w_up;  const void* w_down;
-  const float* s_gate; const float* s_up; const float* s_down;
+  const void* s_gate;  const void* s_up;  const void* s_down;
   const void* sh_gate; const void* sh_up; const void* sh_down;
-  const float* sh_s_gate; const float* sh_s_up; const float* sh_s_down;
+  const void* sh_s_gate; const void* sh_s_up; const void* sh_s_down;
 } moe_expert_weights;
 
 /* Optional routing outputs of moe_forward (any member may be NULL). */

@@ -139,8 +139,8 @@ struct GemmLaunch {
   const void* A;            // [rows, K] bf16 or f32
   const void* B0;           // gate (gated) or down weights
   const void* B1;           // up weights (gated) or null
-  const float* S0;          // fp8 row scales for B0 [groups][n_b] or null
-  const float* S1;
+  const void* S0;           // B0's scales: fp8 f32 row scales [groups][n_b]; INT4 uint32
+  const void* S1;           // group words [groups][n_b][K/128]; else null
   void* out;                // gated: h [rows, F] (bf16 or f32); else y [rows, N] f32
   const int32_t* offsets;   // [groups+1] or null
   int32_t* tile_prefix;     // workspace [2 * (groups+1)]: sanitised offsets, tile prefix
@@ -149,7 +149,7 @@ struct GemmLaunch {
   int64_t max_rows;         // upper bound on rows (grid sizing)
   int K;                    // reduction size
   int N;                    // output columns (F for gated, d for down)
-  int w_dtype;              // MOE_F32 / MOE_BF16 / MOE_FP8_E4M3FN
+  int w_dtype;              // MOE_F32 / MOE_BF16 / MOE_FP8_E4M3FN / MOE_INT4
   bool gated;
   bool shared;              // the shared expert (names its launches apart)
   const int32_t* gather = nullptr;  // row r of A is A[gather[r]] (A = x, gather = src_token), or

@@ -328,7 +328,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 // 128 x 128 kernel (fp8, and bf16 shapes the large tiles do not divide), else
 // the fp32 SIMT kernel.
 // Kernel choice per pass (rows per group estimated as max_rows / groups):
-//   stream (bm 64 or 32): fp8 weights, or bf16 groups of fewer than 128 rows --
+//   stream (bm 64 or 32; INT4 always 32): fp8 and INT4 weights, or bf16 groups of
+//          fewer than 128 rows --
 //          bound by reading the weights, so small tiles and full-line streams;
 //   big (bm 256): bf16 groups of hundreds of rows -- bound by the matrix cores;
 //   128 x 128 kernel: any shape the two do not divide; SIMT kernel for fp32.
@@ -336,8 +337,9 @@ static bool stream_shape_ok(const GemmLaunch& a) {
   return a.K % 128 == 0 && (a.gated ? (a.N % 128 == 0) : (a.N % 256 == 0));
 }
 static int stream_bm(const GemmLaunch& a) {
-  if (a.w_dtype == MOE_F32 || !stream_shape_ok(a)) return 0;
+  if (a.w_dtype == MOE_F32 || !stream_shape_ok(a)) return 0;  // (INT4 shapes always fit: checked with the config)
   const int64_t per_group = ceil_div(a.max_rows, std::max(a.groups, 1));
+  if (a.w_dtype == MOE_INT4) return 32;
   if (a.w_dtype == MOE_BF16 && per_group >= 128) return 0;
   return per_group <= 32 ? 32 : 64;
 }
@@ -409,6 +411,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   const bool big = use_big(a);
   const int sbm = stream_bm(a);
   if (a.gather && !big && !sbm) return fail(MOE_ERR_UNSUPPORTED, "row gather needs the large-tile or streaming GEMM");
+  if (a.w_dtype == MOE_INT4 && !sbm) return fail(MOE_ERR_UNSUPPORTED, "INT4 weights need K %% 128 == 0 and N %% 256 == 0");
   const int bm = f32 ? SM : (big ? 256 : (sbm ? sbm : MB));
   int32_t* goff = a.tile_prefix;
   int32_t* tp = a.tile_prefix + (a.groups + 1);
@@ -420,7 +423,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
 
   if (big) return launch_gemm_bf16_big(a, goff, tp, s);
   if (sbm) return launch_gemm_stream(a, goff, tp, sbm, s);
-  GemmParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
+  GemmParams p{a.A, a.B0, a.B1, (const float*)a.S0, (const float*)a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
   const int64_t mt_upper = ceil_div(a.max_rows, bm) + a.groups;
   if (f32) {
     p.n_tiles = a.gated ? a.N / 32 : a.N / SN;

@@ -117,6 +117,10 @@ moe_status check_config(const moe_config* c) {
     if (c->act_dtype != MOE_BF16)
       return fail(MOE_ERR_UNSUPPORTED, "bf16/fp8 weights need bf16 activations");
     if (c->F % 64) return fail(MOE_ERR_UNSUPPORTED, "F = %d must be a multiple of 64", c->F);
+  } else if (c->w_dtype == MOE_INT4) {
+    if (c->act_dtype != MOE_BF16) return fail(MOE_ERR_UNSUPPORTED, "INT4 weights need bf16 activations");
+    if (c->F % 128 || c->d % 256)
+      return fail(MOE_ERR_UNSUPPORTED, "INT4 weights need F %% 128 == 0 and d %% 256 == 0 (F = %d, d = %d)", c->F, c->d);
   } else {
     return fail(MOE_ERR_INVALID_ARGUMENT, "w_dtype = %d", c->w_dtype);
   }
@@ -154,6 +158,7 @@ int64_t perm_rows(const moe_config* c) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
 struct Layout {
   // router scratch (bf16 path): split weights, logit partials; overlaps the
@@ -230,15 +235,20 @@ moe_status check_weights(const moe_config* c, const moe_expert_weights* w) {
   if (!w->w_gate || !w->w_up || !w->w_down) return fail(MOE_ERR_INVALID_ARGUMENT, "expert weight pointer is NULL");
   if (!aligned16(w->w_gate) || !aligned16(w->w_up) || !aligned16(w->w_down))
     return fail(MOE_ERR_INVALID_ARGUMENT, "expert weights must be 16-byte aligned");
-  const bool fp8 = c->w_dtype == MOE_FP8_E4M3FN;
-  if (fp8 != (w->s_gate && w->s_up && w->s_down) || (!fp8 && (w->s_gate || w->s_up || w->s_down)))
-    return fail(MOE_ERR_INVALID_ARGUMENT, "row scales are required for fp8 weights and only for them");
+  const bool scaled = c->w_dtype == MOE_FP8_E4M3FN || c->w_dtype == MOE_INT4;
+  if (scaled != (w->s_gate && w->s_up && w->s_down) || (!scaled && (w->s_gate || w->s_up || w->s_down)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "scales are required for fp8 and INT4 weights and only for them");
+  if (c->w_dtype == MOE_INT4 && (!aligned4(w->s_gate) || !aligned4(w->s_up) || !aligned4(w->s_down)))
+    return fail(MOE_ERR_INVALID_ARGUMENT, "INT4 group words must be 4-byte aligned");
   if (c->n_shared) {
     if (!w->sh_gate || !w->sh_up || !w->sh_down) return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights missing");
     if (!aligned16(w->sh_gate) || !aligned16(w->sh_up) || !aligned16(w->sh_down))
       return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights must be 16-byte aligned");
-    if (fp8 != (w->sh_s_gate && w->sh_s_up && w->sh_s_down))
-      return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert row scales are required for fp8 weights");
+    if (scaled != (w->sh_s_gate && w->sh_s_up && w->sh_s_down) ||
+        (!scaled && (w->sh_s_gate || w->sh_s_up || w->sh_s_down)))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert scales are required for fp8 and INT4 weights and only for them");
+    if (c->w_dtype == MOE_INT4 && (!aligned4(w->sh_s_gate) || !aligned4(w->sh_s_up) || !aligned4(w->sh_s_down)))
+      return fail(MOE_ERR_INVALID_ARGUMENT, "INT4 group words must be 4-byte aligned");
   } else if (w->sh_gate || w->sh_up || w->sh_down) {
     return fail(MOE_ERR_INVALID_ARGUMENT, "shared expert weights given but n_shared == 0");
   }

@@ -312,6 +312,7 @@ def shrink(shape: MoEShape, T: int, d: int, F: int, name: Optional[str] = None) 
     return shape.replace(name=name or f"{shape.name}_T{T}_d{d}_F{F}", T=T, d=d, F=F)
 
 
-def nbytes_of(dtype: int) -> int:
-    return {DT_F32: 4, DT_BF16: 2, DT_FP8: 1}[dtype]  # (INT4: half a byte, plus group parameters)
+def nbytes_of(dtype: int) -> float:
+    """Bytes per element (INT4: half a byte; its group words are counted apart)."""
+    return {DT_F32: 4, DT_BF16: 2, DT_FP8: 1, DT_INT4: 0.5}[dtype]
 

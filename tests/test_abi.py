@@ -71,6 +71,8 @@ def _cfg(L, **kw):
     (dict(reroute_depth=1, E=128, k=65), 2),
     (dict(n_groups=3), 1), (dict(n_groups=4, topk_groups=0), 1), (dict(n_groups=4, topk_groups=5), 1),
     (dict(n_groups=4, topk_groups=1, k=3), 1), (dict(n_groups=4, topk_groups=1, reroute_depth=1), 1),
+    (dict(w_dtype=W.DT_INT4, d=384), 2), (dict(w_dtype=W.DT_INT4, F=192), 2),
+    (dict(w_dtype=W.DT_INT4, act_dtype=W.DT_F32), 2),
 ])
 def test_invalid_configs_rejected(L, kw, status):
     cfg = _cfg(L, **kw)
@@ -109,6 +111,13 @@ def test_entry_points_validate_before_launch(L):
     w = L.moe_expert_weights(256, 256, 256, None, None, None, None, None, None, None, None, None)
     cfg8 = _cfg(L, w_dtype=W.DT_FP8)
     assert lib.moe_expert_ffn(ctypes.byref(cfg8), dummy, dummy, dummy, ctypes.byref(w), dummy, None,
+                              dummy, 1 << 40, None) == 1
+    # INT4 requires its group words, 4-byte aligned
+    cfg4 = _cfg(L, w_dtype=W.DT_INT4)
+    assert lib.moe_expert_ffn(ctypes.byref(cfg4), dummy, dummy, dummy, ctypes.byref(w), dummy, None,
+                              dummy, 1 << 40, None) == 1
+    w4 = L.moe_expert_weights(256, 256, 256, 512, 512, 514, None, None, None, None, None, None)
+    assert lib.moe_expert_ffn(ctypes.byref(cfg4), dummy, dummy, dummy, ctypes.byref(w4), dummy, None,
                               dummy, 1 << 40, None) == 1
     cfgsh = _cfg(L, n_shared=1)
     assert lib.moe_expert_ffn(ctypes.byref(cfgsh), dummy, dummy, dummy, ctypes.byref(w), dummy, dummy,

@@ -52,6 +52,13 @@ SMALL = {
     "grouped_reroute": WK["mixtral_bf16"].replace(name="grr", T=400, d=128, E=64, k=2, F=128,
                                                   capacity_factor=1.0, reroute_depth=3,
                                                   n_groups=8, topk_groups=2),
+    # group-wise INT4 weights: the decode workload at full size (C = 1), a small
+    # skewed batch with ragged groups, experts of ~125 rows (several 32-row tiles
+    # each), and the fine-grained layer with its shared expert in INT4
+    "int4_decode": WK["skewed_int4_decode"],
+    "int4_small": W.shrink(WK["skewed_int4_decode"], T=300, d=256, F=256),
+    "int4_rows": WK["mixtral_bf16"].replace(name="i4r", T=500, d=256, E=8, k=2, F=384, w_dtype=W.DT_INT4),
+    "int4_shared": W.shrink(WK["fine_shared_bf16"], T=150, d=256, F=128).replace(w_dtype=W.DT_INT4),
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
