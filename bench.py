@@ -6,8 +6,10 @@ input already resident in HBM.  Prints one JSON line:
 
   value       tokens per second of the whole layer (T / step time)
   roofline    the dominant kernel's achieved rate from HIP events recorded
-              around each launch on its stream during the timed steps, against
-              the MI355X peak for its bound
+              around each launch on its stream, against the MI355X peak for
+              its bound; the events are taken over a second run of the same K
+              steps right after the timed one (recording them between kernels
+              would lengthen the timed steps themselves)
   kernels     the same for every kernel of the step (average duration,
               algorithmic FLOP or bytes per launch, rate, fraction of peak)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
@@ -222,14 +224,21 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    L.moe_profile_read()  # discard anything recorded before
-    L.moe_profile_enable(True)
+    # timed region: K steps, one event between steps and none inside them
     marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     marks[0].record()
     for i in range(args.steps):
         step(args.warmup + i)
         marks[i + 1].record()
+    torch.cuda.synchronize()
+    # per-kernel durations: the same K steps again, with the library's event pair
+    # around every launch on its stream (events between kernels lengthen a
+    # decode-sized step by up to 75 %, so they stay out of the timed region)
+    L.moe_profile_read()  # discard anything recorded before
+    L.moe_profile_enable(True)
+    for i in range(args.steps):
+        step(args.warmup + args.steps + i)
     torch.cuda.synchronize()
     L.moe_profile_enable(False)
     prof = L.moe_profile_read()

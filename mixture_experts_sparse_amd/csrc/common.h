@@ -55,6 +55,23 @@ __device__ __forceinline__ void fp8x16_to_bf16x16(const uint4& q, uint4& lo, uin
   hi.w = fp8x2_to_bf16x2<true>(q.w);
 }
 
+// 8 INT4 codes (one 32-bit word: even k in the low nibble of each byte) as the
+// bf16 values 128 + q, in k order.  v_perm_b32 picks bytes of {S0, S1} (S1 =
+// bytes 0-3, S0 = bytes 4-7) by selector.
+__device__ __forceinline__ bf16x8_t int4_frag(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;                   // q0 q2 q4 q6 (bytes)
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;            // q1 q3 q5 q7
+  const uint32_t x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // q0 q1 q2 q3
+  const uint32_t y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // q4 q5 q6 q7
+  constexpr uint32_t C = 0x43434343u;                    // bf16 128 = 0x4300
+  uint4 o;
+  o.x = __builtin_amdgcn_perm(C, x, 0x04010400u);        // [q0, 43, q1, 43]
+  o.y = __builtin_amdgcn_perm(C, x, 0x04030402u);        // [q2, 43, q3, 43]
+  o.z = __builtin_amdgcn_perm(C, y, 0x04010400u);
+  o.w = __builtin_amdgcn_perm(C, y, 0x04030402u);
+  return __builtin_bit_cast(bf16x8_t, o);
+}
+
 __device__ __forceinline__ float silu_f32(float g) { return g / (1.0f + __expf(-g)); }
 
 // ---------------------------------------------------------------- host side
@@ -143,7 +160,8 @@ struct GemmLaunch {
   const void* S1;           // group words [groups][n_b][K/128]; else null
   void* out;                // gated: h [rows, F] (bf16 or f32); else y [rows, N] f32
   const int32_t* offsets;   // [groups+1] or null
-  int32_t* tile_prefix;     // workspace [2 * (groups+1)]: sanitised offsets, tile prefix
+  int32_t* tile_prefix;     // workspace [2 * (groups+1) + ceil(max_rows/16) + groups]: sanitised
+                            // offsets, tile prefix, group of each m-tile (tile_list_ints)
   int groups;
   int single_rows;          // rows when offsets == null
   int64_t max_rows;         // upper bound on rows (grid sizing)
@@ -159,6 +177,10 @@ struct GemmLaunch {
   size_t split_stride = 0;  // elements
 };
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+// int32 entries of GemmLaunch::tile_prefix for `groups` groups of at most `max_rows` rows in all
+inline int64_t tile_list_ints(int groups, int64_t max_rows) {
+  return 2 * (int64_t)(groups + 1) + (max_rows + 15) / 16 + groups;
+}
 // whether the kernel launch_grouped_gemm picks for `a` can read A through a.gather
 // (row byte offsets into A must also fit 32 bits: A_rows * K * 2 < 2^32)
 bool gather_ok(const GemmLaunch& a, int64_t a_rows);

@@ -32,7 +32,8 @@ namespace {
 
 // ---------------------------------------------------------------- tile list
 // goff[g] = running max of clamp(offsets[g], 0, max_rows); tiles[g] = ceil(rows/bm);
-// tile_prefix = exclusive scan of tiles.  groups + 1 <= 512.
+// tile_prefix = exclusive scan of tiles, then the group of every m-tile.
+// groups + 1 <= 512.
 __global__ __launch_bounds__(512) void tiles_kernel(const int32_t* __restrict__ offsets, int groups,
                                                     int single_rows, int64_t max_rows, int bm,
                                                     int32_t* __restrict__ goff,
@@ -70,6 +71,13 @@ __global__ __launch_bounds__(512) void tiles_kernel(const int32_t* __restrict__ 
   if (i <= groups) {
     goff[i] = o[i];
     tile_prefix[i] = (i == 0) ? 0 : tp[i - 1];
+  }
+  // the group of each m-tile (group-major order), after the prefix: map_tile
+  // finds a tile's group with one load instead of a search over the prefix
+  if (i < groups) {
+    int32_t* tile_group = tile_prefix + groups + 1;
+    const int first = (i == 0) ? 0 : tp[i - 1];
+    for (int m = first; m < tp[i]; ++m) tile_group[m] = i;
   }
 }
 
@@ -331,6 +339,8 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmParams p) {
 //   stream (bm 64 or 32; INT4 always 32): fp8 and INT4 weights, or bf16 groups of
 //          fewer than 128 rows --
 //          bound by reading the weights, so small tiles and full-line streams;
+//          groups of at most 16 rows (decode) take bm 16 with K split over the
+//          waves of a block, four times the blocks in flight;
 //   big (bm 256): bf16 groups of hundreds of rows -- bound by the matrix cores;
 //   128 x 128 kernel: any shape the two do not divide; SIMT kernel for fp32.
 static bool stream_shape_ok(const GemmLaunch& a) {
@@ -339,6 +349,7 @@ static bool stream_shape_ok(const GemmLaunch& a) {
 static int stream_bm(const GemmLaunch& a) {
   if (a.w_dtype == MOE_F32 || !stream_shape_ok(a)) return 0;  // (INT4 shapes always fit: checked with the config)
   const int64_t per_group = ceil_div(a.max_rows, std::max(a.groups, 1));
+  if (per_group <= 16) return 16;  // K split over the waves of a block
   if (a.w_dtype == MOE_INT4) return 32;
   if (a.w_dtype == MOE_BF16 && per_group >= 128) return 0;
   return per_group <= 32 ? 32 : 64;
@@ -422,6 +433,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   if (st != MOE_OK) return st;
 
   if (big) return launch_gemm_bf16_big(a, goff, tp, s);
+  if (sbm == 16) return launch_gemm_ksplit(a, goff, tp, s);
   if (sbm) return launch_gemm_stream(a, goff, tp, sbm, s);
   GemmParams p{a.A, a.B0, a.B1, (const float*)a.S0, (const float*)a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0};
   const int64_t mt_upper = ceil_div(a.max_rows, bm) + a.groups;

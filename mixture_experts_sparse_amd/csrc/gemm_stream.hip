@@ -36,6 +36,7 @@
 //     acc += scale * (t - (128 + zero) * rowsum)
 // applies the group's parameters once per step and output element.
 #include <algorithm>
+#include <type_traits>
 
 #include "grouped.h"
 
@@ -61,6 +62,13 @@ __device__ __forceinline__ void block_sync() {
 // waits count loads in flight newest first, so load groups must issue in the
 // order written.
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
+
+// Steps of the main loop vs the steps after it.  A step's wait counts the loads
+// issued behind the ones it needs: the next step's activations and, in the main
+// loop, a full group of weight prefetches.  Past the main loop those prefetches
+// feed no step, the compiler removes them, and the count must leave them out.
+constexpr std::integral_constant<bool, false> kBody{};
+constexpr std::integral_constant<bool, true> kTailStep{};
 
 struct StreamParams {
   const void* A;
@@ -176,11 +184,14 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
     uint4 b0[NF][RAW], b1[NF][RAW], b2[NF][RAW], b3[NF][RAW];
 
     // one K step: weights of `ks` in cur; weights of ks + PD requested into ahead
-    auto step = [&](int ks, uint4 (&cur)[NF][RAW], uint4 (&ahead)[NF][RAW]) {
+    // (tail steps: the compiler drops their prefetches, which no step reads, so
+    // the wait there counts only the activation loads behind this step's)
+    auto step = [&](int ks, uint4 (&cur)[NF][RAW], uint4 (&ahead)[NF][RAW], auto tail) {
+      constexpr bool kTail = decltype(tail)::value;
       // landed: activations and weights of step ks; still in flight, newest
       // first: activations of ks + 1 and weights of ks + PD - 1 (issued one step
       // ago), and for PD = 3 the weights of ks + 1 .. ks + 2 are older than those
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_INS + (PD > 1 ? NB : 0)));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_INS + (PD > 1 && !kTail ? NB : 0)));
       // this wave's LDS reads of step ks - 1 are complete before the barrier:
       // after it, another wave may refill that stage
       __builtin_amdgcn_s_waitcnt(kLgkm0);
@@ -221,14 +232,14 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       issue_fence();
       // ring of four: step k computes from b[k % 4] and refills b[(k + 3) % 4]
       for (; ks + 3 < ksteps; ks += 4) {
-        step(ks, b0, b3);
-        step(ks + 1, b1, b0);
-        step(ks + 2, b2, b1);
-        step(ks + 3, b3, b2);
+        step(ks, b0, b3, kBody);
+        step(ks + 1, b1, b0, kBody);
+        step(ks + 2, b2, b1, kBody);
+        step(ks + 3, b3, b2, kBody);
       }
-      if (ks < ksteps) step(ks, b0, b3);
-      if (ks + 1 < ksteps) step(ks + 1, b1, b0);
-      if (ks + 2 < ksteps) step(ks + 2, b2, b1);
+      if (ks < ksteps) step(ks, b0, b3, kTailStep);
+      if (ks + 1 < ksteps) step(ks + 1, b1, b0, kTailStep);
+      if (ks + 2 < ksteps) step(ks + 2, b2, b1, kTailStep);
     } else {
       issue_a(0);
       issue_fence();
@@ -238,10 +249,10 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       issue_fence();
       // pairs of steps so the weight double buffer swaps roles statically
       for (; ks + 1 < ksteps; ks += 2) {
-        step(ks, b0, b1);
-        step(ks + 1, b1, b0);
+        step(ks, b0, b1, kBody);
+        step(ks + 1, b1, b0, kBody);
       }
-      if (ks < ksteps) step(ks, b0, b1);
+      if (ks < ksteps) step(ks, b0, b1, kTailStep);
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
 
@@ -279,23 +290,6 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       }
     }
   }
-}
-
-// 8 INT4 codes (one 32-bit word: even k in the low nibble of each byte) as the
-// bf16 values 128 + q, in k order.  v_perm_b32 picks bytes of {S0, S1} (S1 =
-// bytes 0-3, S0 = bytes 4-7) by selector.
-__device__ __forceinline__ bf16x8_t int4_frag(uint32_t w) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;                   // q0 q2 q4 q6 (bytes)
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;            // q1 q3 q5 q7
-  const uint32_t x = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // q0 q1 q2 q3
-  const uint32_t y = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // q4 q5 q6 q7
-  constexpr uint32_t C = 0x43434343u;                    // bf16 128 = 0x4300
-  uint4 o;
-  o.x = __builtin_amdgcn_perm(C, x, 0x04010400u);        // [q0, 43, q1, 43]
-  o.y = __builtin_amdgcn_perm(C, x, 0x04030402u);        // [q2, 43, q3, 43]
-  o.z = __builtin_amdgcn_perm(C, y, 0x04010400u);
-  o.w = __builtin_amdgcn_perm(C, y, 0x04030402u);
-  return __builtin_bit_cast(bf16x8_t, o);
 }
 
 template <bool GATED, int MF>
@@ -384,10 +378,12 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_int4_kernel(StreamParams p
 
     // one K step (= one group): codes and words of `ks` in cw / cq; those of
     // ks + PD requested into nw / nq
-    auto step = [&](int ks, const uint4 (&cw)[NF], const uint32_t (&cq)[NF], uint4 (&nw)[NF], uint32_t (&nq)[NF]) {
+    auto step = [&](int ks, const uint4 (&cw)[NF], const uint32_t (&cq)[NF], uint4 (&nw)[NF], uint32_t (&nq)[NF],
+                    auto tail) {
+      constexpr bool kTail = decltype(tail)::value;
       // landed: everything but the newest loads -- the weights of ks + PD - 1 and
       // the activations of ks + 1, both issued one step ago
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_INS + NBI));
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(A_INS + (kTail ? 0 : NBI)));
       __builtin_amdgcn_s_waitcnt(kLgkm0);
       block_sync();
       load_w(nw, nq, ks + PD);
@@ -442,11 +438,11 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_int4_kernel(StreamParams p
     int ks = 0;
     for (; ks + R <= ksteps; ks += R) {
 #pragma unroll
-      for (int u = 0; u < R; ++u) step(ks + u, wr[u], qr[u], wr[(u + PD) % R], qr[(u + PD) % R]);
+      for (int u = 0; u < R; ++u) step(ks + u, wr[u], qr[u], wr[(u + PD) % R], qr[(u + PD) % R], kBody);
     }
 #pragma unroll
     for (int u = 0; u < R - 1; ++u)
-      if (ks + u < ksteps) step(ks + u, wr[u], qr[u], wr[(u + PD) % R], qr[(u + PD) % R]);
+      if (ks + u < ksteps) step(ks + u, wr[u], qr[u], wr[(u + PD) % R], qr[(u + PD) % R], kTailStep);
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
 
     // ---- epilogue (rows past the group's end are not stored)

@@ -11,16 +11,13 @@ struct TileRef {
 
 // Map a linear tile index L (ordered group-major, then n-tile, then m-tile) to
 // (group, n-tile, first row, valid rows).  tp = exclusive prefix of m-tiles per
-// group, goff = sanitised row offsets; both built by tiles_kernel.
+// group followed by the group of each m-tile, goff = sanitised row offsets; all
+// built by tiles_kernel.  Group g's tiles are L in [tp[g], tp[g+1]) * n_tiles,
+// so L / n_tiles is one of g's m-tile slots and the table names g directly.
 __device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int bm,
                                             const int32_t* __restrict__ tp,
                                             const int32_t* __restrict__ goff) {
-  int lo = 0, hi = groups;  // largest g with n_tiles * tp[g] <= L
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)tp[mid] * n_tiles <= L) lo = mid; else hi = mid;
-  }
-  const int g = lo;
+  const int g = tp[groups + 1 + L / n_tiles];
   const int mt = tp[g + 1] - tp[g];
   const int local = L - tp[g] * n_tiles;
   const int nt = local / mt, mi = local % mt;
@@ -38,5 +35,9 @@ moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const 
 // weight-streaming grouped GEMM for groups of few rows (gemm_stream.hip): bf16 or
 // fp8 weights, bm = 32 or 64 rows per tile, 256 weight rows per block
 moe_status launch_gemm_stream(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, int bm, hipStream_t s);
+
+// weight-streaming grouped GEMM for groups of at most 16 rows (gemm_ksplit.hip):
+// 16-row tiles, the block's four waves split K
+moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s);
 
 }  // namespace moe

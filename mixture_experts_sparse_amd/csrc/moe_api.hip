@@ -196,8 +196,8 @@ Layout layout_of(const moe_config* c) {
   L.hist = take(sizeof(int32_t) * nblk * c->E);
   L.reroute = take(c->reroute_depth > 0 ? sizeof(int32_t) * (2 * (size_t)P + c->E + 1) : 0);
   L.perm_end = o;
-  L.tiles = take(sizeof(int32_t) * 2 * (c->E + 1));
-  L.tiles_sh = take(sizeof(int32_t) * 4);
+  L.tiles = take(sizeof(int32_t) * tile_list_ints(c->E, R));
+  L.tiles_sh = take(sizeof(int32_t) * tile_list_ints(1, c->T));
   L.h = take(hb * R * c->F);
   L.h_sh = take(c->n_shared ? hb * (size_t)c->T * c->F : 0);
   L.split = down_split_k(R, c->E, c->F, c->d, c->w_dtype);

@@ -27,7 +27,11 @@ SMALL = {
     "bf16_skewed_big": WK["mixtral_bf16"].replace(name="bf16z", T=800, d=256, E=8, k=2, F=256,
                                                   bias_mode=W.BIAS_LOGIT, bias_kind="zipf1.2"),
     "skewed_fp8_decode": WK["skewed_fp8_decode"],
-    # decode-sized bf16 batch: the streaming GEMM with half-width blocks
+    # 17-32 rows per expert: the streaming GEMM with 32-row tiles (fewer rows per
+    # expert take the K-split kernel, more take 64-row tiles or the large tiles)
+    "fp8_stream32": W.shrink(WK["skewed_fp8"], T=1500, d=256, F=256),
+    "bf16_stream32": WK["mixtral_bf16"].replace(name="bf16s32", T=200, d=512, E=16, k=2, F=256),
+    # decode-sized bf16 batch (8 rows per expert): the K-split GEMM
     "bf16_decode": WK["mixtral_bf16"].replace(name="bf16d", T=64, d=512, E=16, k=2, F=256),
     # overflow re-routing: fp8 skewed (streaming GEMM), bf16 Zipf (large-tile GEMM),
     # k = 8 sigmoid, odd k = 3, decode size (C = 1), fp32
