@@ -172,11 +172,15 @@ struct GemmLaunch {
   bool shared;              // the shared expert (names its launches apart)
   const int32_t* gather = nullptr;  // row r of A is A[gather[r]] (A = x, gather = src_token), or
                                     // null for a dense A; only kernels that gather_ok() admits
+  bool tiles_ready = false; // tile_prefix already holds this launch's tile lists (same
+                            // offsets, groups, max_rows and tile height as a previous launch)
   int split_k = 1;          // down pass: K split into parts; part 0 goes to `out`,
   float* split_rest = nullptr;  // part p >= 1 to split_rest + (p - 1) * split_stride
   size_t split_stride = 0;  // elements
 };
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+// rows per tile of the kernel launch_grouped_gemm picks for `a`
+int grouped_gemm_bm(const GemmLaunch& a);
 // int32 entries of GemmLaunch::tile_prefix for `groups` groups of at most `max_rows` rows in all
 inline int64_t tile_list_ints(int groups, int64_t max_rows) {
   return 2 * (int64_t)(groups + 1) + (max_rows + 15) / 16 + groups;

@@ -417,20 +417,31 @@ bool gather_ok(const GemmLaunch& a, int64_t a_rows) {
   return a_rows * (int64_t)a.K * 2 < ((int64_t)1 << 32);
 }
 
+int grouped_gemm_bm(const GemmLaunch& a) {
+  if (a.w_dtype == MOE_F32) return SM;
+  if (use_big(a)) return 256;
+  const int sbm = stream_bm(a);
+  return sbm ? sbm : MB;
+}
+
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   const bool f32 = (a.w_dtype == MOE_F32);
   const bool big = use_big(a);
   const int sbm = stream_bm(a);
   if (a.gather && !big && !sbm) return fail(MOE_ERR_UNSUPPORTED, "row gather needs the large-tile or streaming GEMM");
   if (a.w_dtype == MOE_INT4 && !sbm) return fail(MOE_ERR_UNSUPPORTED, "INT4 weights need K %% 128 == 0 and N %% 256 == 0");
-  const int bm = f32 ? SM : (big ? 256 : (sbm ? sbm : MB));
+  const int bm = grouped_gemm_bm(a);
   int32_t* goff = a.tile_prefix;
   int32_t* tp = a.tile_prefix + (a.groups + 1);
-  int tok = begin_launch("gemm_tiles", s);
-  hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(512), 0, s, a.offsets, a.groups, a.single_rows,
-                     a.max_rows, bm, goff, tp);
-  moe_status st = end_launch(tok, s);
-  if (st != MOE_OK) return st;
+  moe_status st;
+  int tok;
+  if (!a.tiles_ready) {
+    tok = begin_launch("gemm_tiles", s);
+    hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(512), 0, s, a.offsets, a.groups, a.single_rows,
+                       a.max_rows, bm, goff, tp);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+  }
 
   if (big) return launch_gemm_bf16_big(a, goff, tp, s);
   if (sbm == 16) return launch_gemm_ksplit(a, goff, tp, s);

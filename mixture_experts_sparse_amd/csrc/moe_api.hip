@@ -323,9 +323,11 @@ moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const
   GemmLaunch g = gate_up_launch(c, x, x_perm, gather, offsets, w, ws);
   moe_status st = launch_grouped_gemm(g, s);
   if (st != MOE_OK) return st;
+  const int bm_gate_up = grouped_gemm_bm(g);
   g.A = ws + L.h; g.gather = nullptr; g.B0 = w->w_down; g.B1 = nullptr; g.S0 = w->s_down; g.S1 = nullptr;
   g.out = y_perm; g.K = c->F; g.N = c->d; g.gated = false;
   g.split_k = L.split; g.split_rest = (float*)(ws + L.y_rest); g.split_stride = (size_t)R * c->d;
+  g.tiles_ready = grouped_gemm_bm(g) == bm_gate_up;  // same offsets and rows: reuse the tile lists
   st = launch_grouped_gemm(g, s);
   if (st == MOE_OK && reduce_partials)
     st = launch_sum_partials(y_perm, (const float*)(ws + L.y_rest), (size_t)R * c->d, L.split, offsets, c->E, R,
@@ -335,11 +337,13 @@ moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const
   g.A = x; g.B0 = w->sh_gate; g.B1 = w->sh_up; g.S0 = w->sh_s_gate; g.S1 = w->sh_s_up;
   g.out = ws + L.h_sh; g.offsets = nullptr; g.tile_prefix = (int32_t*)(ws + L.tiles_sh);
   g.groups = 1; g.single_rows = c->T; g.max_rows = c->T; g.K = c->d; g.N = c->F; g.gated = true;
-  g.shared = true;
+  g.shared = true; g.tiles_ready = false; g.split_k = 1;
   st = launch_grouped_gemm(g, s);
   if (st != MOE_OK) return st;
+  const int bm_sh = grouped_gemm_bm(g);
   g.A = ws + L.h_sh; g.B0 = w->sh_down; g.B1 = nullptr; g.S0 = w->sh_s_down; g.S1 = nullptr;
   g.out = y_shared; g.K = c->F; g.N = c->d; g.gated = false;
+  g.tiles_ready = grouped_gemm_bm(g) == bm_sh;
   g.split_k = L.split_sh; g.split_rest = (float*)(ws + L.y_sh_rest); g.split_stride = (size_t)c->T * c->d;
   st = launch_grouped_gemm(g, s);
   if (st == MOE_OK && reduce_partials)

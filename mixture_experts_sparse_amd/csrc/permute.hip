@@ -8,7 +8,8 @@
 // into one contiguous block so the expert runs one matmul over them.
 //
 // Pairs p = t*k + j are split into chunks of kPermChunk.  Three small kernels
-// compute the same counting sort a sequential walk over p would:
+// (one, count_rank_kernel, when all pairs fit one chunk) compute the same
+// counting sort a sequential walk over p would:
 //   hist : per-chunk per-expert counts (LDS atomics; only counts, no order)
 //   scan : per expert, exclusive scan over chunks -> chunk base ranks, counts,
 //          kept = min(counts, C), offsets, n_dropped
@@ -87,24 +88,14 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(int32_t* __restrict__ hi
   }
 }
 
-__global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ base,
-                                                        const int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ dest_row,
-                                                        int32_t* __restrict__ src_token,
-                                                        int P, int E, int k, int ld, int64_t cap,
-                                                        int64_t rows) {
-  __shared__ int running[256];
-  __shared__ int wcnt[4][256];
+// Stable ranks of the pairs [p0, p1) given running[e] = pairs of expert e before
+// p0 (LDS, updated as the chunk is walked) and the kept-row offsets `off` (global
+// or LDS): rank = running + lanes of earlier waves + earlier lanes of this wave
+// with the same expert (found bit by bit from ballots); kept iff rank < cap.
+__device__ __forceinline__ void rank_pairs(const int32_t* __restrict__ idx, int p0, int p1, int E, int k, int ld,
+                                           int64_t cap, const int32_t* off, int* running, int (*wcnt)[256],
+                                           int32_t* __restrict__ dest_row, int32_t* __restrict__ src_token) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < 256; e += kThreads) {
-    running[e] = (e < E) ? base[(size_t)blockIdx.x * E + e] : 0;
-    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
-  }
-  const int n_rows = offsets[E];
-  __syncthreads();
-  const int p0 = blockIdx.x * kPermChunk;
-  const int p1 = min(p0 + kPermChunk, P);
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   for (int r0 = p0; r0 < p1; r0 += kThreads) {  // uniform trip count in the block
     const int p = r0 + tid;
@@ -126,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
       int r = running[e] + before;
       for (int w = 0; w < wave; ++w) r += wcnt[w][e];
       if (cap < 0 || (int64_t)r < cap) {
-        const int row = offsets[e] + r;
+        const int row = off[e] + r;
         dest_row[p] = row;
         src_token[row] = p / k;
       } else {
@@ -140,10 +131,90 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restric
     }
     __syncthreads();
   }
+}
+
+__global__ __launch_bounds__(kThreads) void rank_kernel(const int32_t* __restrict__ idx,
+                                                        const int32_t* __restrict__ base,
+                                                        const int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ dest_row,
+                                                        int32_t* __restrict__ src_token,
+                                                        int P, int E, int k, int ld, int64_t cap,
+                                                        int64_t rows) {
+  __shared__ int running[256];
+  __shared__ int wcnt[4][256];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < 256; e += kThreads) {
+    running[e] = (e < E) ? base[(size_t)blockIdx.x * E + e] : 0;
+    wcnt[0][e] = wcnt[1][e] = wcnt[2][e] = wcnt[3][e] = 0;
+  }
+  const int n_rows = offsets[E];
+  __syncthreads();
+  const int p0 = blockIdx.x * kPermChunk;
+  const int p1 = min(p0 + kPermChunk, P);
+  rank_pairs(idx, p0, p1, E, k, ld, cap, offsets, running, wcnt, dest_row, src_token);
   // rows past the kept ones carry no token; block b clears rows [p0, p0 + chunk)
   // (rows <= P, so the chunks cover every row; kept rows are written above by
   // whichever block owns the pair, and are < n_rows, so the writes are disjoint)
   for (int64_t r = (int64_t)p0 + tid; r < (int64_t)p0 + kPermChunk && r < rows; r += kThreads)
+    if (r >= n_rows) src_token[r] = -1;
+}
+
+// All pairs in one chunk (P <= kPermChunk, decode-sized batches): the
+// histogram, the offsets and the ranks of hist_kernel, scan_kernel and
+// rank_kernel in one block, so a small batch pays one launch instead of three.
+__global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                              int k, int ld, int64_t cap, int64_t rows,
+                                                              int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ n_dropped,
+                                                              int32_t* __restrict__ stats,
+                                                              int32_t* __restrict__ dest_row,
+                                                              int32_t* __restrict__ src_token) {
+  __shared__ int running[256];
+  __shared__ int wcnt[4][256];
+  __shared__ int kept_s[256];
+  __shared__ int drop_s[256];
+  __shared__ int32_t off_s[257];
+  const int tid = threadIdx.x;
+  running[tid] = 0;
+  wcnt[0][tid] = wcnt[1][tid] = wcnt[2][tid] = wcnt[3][tid] = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += kThreads) {
+    const int e = pair_expert(idx, p, k, ld);
+    if (e >= 0 && e < E) atomicAdd(&running[e], 1);  // ids outside [0,E) are ignored
+  }
+  __syncthreads();
+  const int e = tid;
+  const int run = (e < E) ? running[e] : 0;
+  const int kept = (e < E) ? (int)((cap >= 0 && (int64_t)run > cap) ? cap : run) : 0;
+  kept_s[e] = kept;
+  drop_s[e] = run - kept;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive scans of kept and dropped
+    const int v = (e >= off) ? kept_s[e - off] : 0;
+    const int dv = (e >= off) ? drop_s[e - off] : 0;
+    __syncthreads();
+    kept_s[e] += v;
+    drop_s[e] += dv;
+    __syncthreads();
+  }
+  if (e < E) {
+    counts[e] = run;
+    offsets[e + 1] = kept_s[e];
+    off_s[e + 1] = kept_s[e];
+    if (stats) { stats[e] = run; stats[E + e] = kept; }
+  }
+  if (e == 0) {
+    offsets[0] = 0;
+    off_s[0] = 0;
+    n_dropped[0] = drop_s[255];
+    if (stats) stats[2 * E] = drop_s[255];
+  }
+  running[e] = 0;  // ranks start at zero in the only chunk
+  __syncthreads();
+  const int n_rows = off_s[E];
+  rank_pairs(idx, 0, P, E, k, ld, cap, off_s, running, wcnt, dest_row, src_token);
+  for (int64_t r = tid; r < rows; r += kThreads)
     if (r >= n_rows) src_token[r] = -1;
 }
 
@@ -378,22 +449,32 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
     return end_launch(tok, s);
   }
   const int ld = a.k + a.fb;
-  int tok = begin_launch("permute_hist", s);
-  hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, P, a.E, a.k, ld);
-  moe_status st = end_launch(tok, s);
-  if (st != MOE_OK) return st;
+  int tok;
+  moe_status st;
+  if (nblk == 1) {
+    tok = begin_launch("permute_count_rank", s);
+    hipLaunchKernelGGL(count_rank_kernel, dim3(1), dim3(kThreads), 0, s, a.topk_idx, P, a.E, a.k, ld, a.capacity,
+                       a.rows, a.counts, a.offsets, a.n_dropped, a.stats, a.dest_row, a.src_token);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+  } else {
+    tok = begin_launch("permute_hist", s);
+    hipLaunchKernelGGL(hist_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, P, a.E, a.k, ld);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
 
-  tok = begin_launch("permute_scan", s);
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, s, a.hist, nblk, a.E, a.capacity,
-                     a.counts, a.offsets, a.n_dropped, a.stats);
-  st = end_launch(tok, s);
-  if (st != MOE_OK) return st;
+    tok = begin_launch("permute_scan", s);
+    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, s, a.hist, nblk, a.E, a.capacity,
+                       a.counts, a.offsets, a.n_dropped, a.stats);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
 
-  tok = begin_launch("permute_rank", s);
-  hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, a.offsets,
-                     a.dest_row, a.src_token, P, a.E, a.k, ld, a.capacity, a.rows);
-  st = end_launch(tok, s);
-  if (st != MOE_OK) return st;
+    tok = begin_launch("permute_rank", s);
+    hipLaunchKernelGGL(rank_kernel, dim3(nblk), dim3(kThreads), 0, s, a.topk_idx, a.hist, a.offsets,
+                       a.dest_row, a.src_token, P, a.E, a.k, ld, a.capacity, a.rows);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+  }
 
   if (a.fb > 0 && a.capacity >= 0) {
     int32_t* re_e = a.reroute;
