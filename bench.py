@@ -274,7 +274,13 @@ def main():
     dk = kernels[dom]
     rec = recorded_traffic(dom, sh.name)
     traffic = None if rec is None else rec["bytes_per_launch"]
-    if "tflops" in dk and ("gate_up" in dom or "down" in dom):
+    # the bound is the roof the kernel's own work meets first: its FLOP at the
+    # MFMA peak against its bytes at the HBM peak (decode-sized GEMMs stream
+    # weights and are HBM-bound; the large-batch ones are MFMA-bound)
+    wk = work.get(kernel_key(dom), {})
+    t_mfma = wk.get("flop", 0.0) / (mfma_peak * 1e12)
+    t_hbm = wk.get("bytes", 0) / (PEAK_HBM_GBS * 1e9)
+    if "tflops" in dk and t_mfma >= t_hbm:
         roof = {"kernel": dom, "bound": "mfma", "achieved": dk["tflops"], "peak": mfma_peak,
                 "unit": "TFLOP/s", "frac": dk["mfma_frac"], "traffic": traffic}
     else:
