@@ -323,6 +323,9 @@ __global__ __launch_bounds__(256) void route_kernel(RouteLaunch a) {
 #define MOE_GPTR(p) ((const __attribute__((address_space(1))) void*)(p))
 #define MOE_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
 
+// LDS a one-token-block router may hold its whole split d-slice in (dynamic LDS)
+constexpr size_t kFusedRouterLds = 96 * 1024;
+
 __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -452,6 +455,118 @@ __global__ __launch_bounds__(512, 1) void router_mfma_kernel(RouterParams p) {
     }
 }
 
+// One token block (T <= 256): the same partial logits as router_prep_kernel +
+// router_mfma_kernel in one launch.  The block splits its own d-slice of W_r
+// (the same exact hi + mid + lo bf16 split, from f32 rows read coalesced along
+// the experts) into LDS, laid out as router_mfma_kernel's stages one after the
+// other, then runs the same MFMA loop over them in the same order -- so the
+// partials are bit-identical to the two-kernel path.
+template <int EP>
+__global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __restrict__ x,
+                                                              const float* __restrict__ w, float* __restrict__ part,
+                                                              int T, int d, int E, int kslice) {
+  constexpr int NF = EP / 16;
+  constexpr int ROWS = 3 * EP;          // B rows: split-major (hi, mid, lo)
+  constexpr int STAGE = ROWS * 64;      // 32 k (64 bytes) per row
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kb = blockIdx.y * kslice, ksteps = kslice / 32;
+  // ---- split W_r[kb .. kb + kslice)[e] into stage ks = k / 32, row (plane EP + e),
+  // 16-byte chunk c = (k % 32) / 8 at slot c ^ ((row >> 1) & 3)
+  // (the LDS bound caps kslice * EP at 16384: at most four 8-k chunks per thread,
+  // whose 32 loads all go out before any is used)
+  const int nchunks = kslice / 8;
+  float wv8[4][8];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int it = tid + u * 512;
+    const int e = it % EP, kc = it / EP;  // experts fastest: the f32 reads coalesce
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      wv8[u][q] = (it < nchunks * EP && e < E) ? w[(size_t)(kb + kc * 8 + q) * E + e] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int it = tid + u * 512;
+    if (it >= nchunks * EP) break;
+    const int e = it % EP, kc = it / EP;
+    uint32_t hi[4], mid[4], lo[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t h2 = 0, m2 = 0, l2 = 0;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float v = wv8[u][q * 2 + h];
+        const uint16_t bh = f32_to_bf16_rne(v);
+        const float r1 = v - bf16_bits_to_f32(bh);
+        const uint16_t bm = f32_to_bf16_rne(r1);
+        const float r2 = r1 - bf16_bits_to_f32(bm);
+        const uint16_t bl = f32_to_bf16_rne(r2);
+        h2 |= (uint32_t)bh << (16 * h);
+        m2 |= (uint32_t)bm << (16 * h);
+        l2 |= (uint32_t)bl << (16 * h);
+      }
+      hi[q] = h2; mid[q] = m2; lo[q] = l2;
+    }
+    const int ks = kc / 4, c = kc % 4;
+    uint8_t* st = smem + (size_t)ks * STAGE;
+#pragma unroll
+    for (int pl = 0; pl < 3; ++pl) {
+      const int row = pl * EP + e;
+      const uint4 v = pl == 0 ? make_uint4(hi[0], hi[1], hi[2], hi[3])
+                    : pl == 1 ? make_uint4(mid[0], mid[1], mid[2], mid[3])
+                              : make_uint4(lo[0], lo[1], lo[2], lo[3]);
+      *(uint4*)(st + row * 64 + ((c ^ ((row >> 1) & 3)) * 16)) = v;
+    }
+  }
+  // ---- the MFMA loop of router_mfma_kernel over the resident stages
+  const int kg = lane >> 4;
+  const uint16_t* xa0 = x + (size_t)min(wv * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const uint16_t* xa1 = x + (size_t)min(wv * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const uint32_t bfrag = (uint32_t)((lane & 15) * 64 + ((kg ^ (((lane & 15) >> 1) & 3)) * 16));
+  f32x4_t acc[2][NF];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < NF; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  bf16x8_t a0 = *(const bf16x8_t*)xa0, a1 = *(const bf16x8_t*)xa1;
+  __syncthreads();  // the split slice is in LDS
+  for (int ks = 0; ks < ksteps; ++ks) {
+    bf16x8_t n0 = a0, n1 = a1;
+    if (ks + 1 < ksteps) {
+      n0 = *(const bf16x8_t*)(xa0 + (ks + 1) * 32);
+      n1 = *(const bf16x8_t*)(xa1 + (ks + 1) * 32);
+    }
+    const uint8_t* st = smem + (size_t)ks * STAGE;
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+      const bf16x8_t bh = *(const bf16x8_t*)(st + bfrag + (n * 16) * 64);
+      const bf16x8_t bm = *(const bf16x8_t*)(st + bfrag + (EP + n * 16) * 64);
+      const bf16x8_t bl = *(const bf16x8_t*)(st + bfrag + (2 * EP + n * 16) * 64);
+      acc[0][n] = mfma16x16x32(a0, bh, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bh, acc[1][n]);
+      acc[0][n] = mfma16x16x32(a0, bm, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bm, acc[1][n]);
+      acc[0][n] = mfma16x16x32(a0, bl, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bl, acc[1][n]);
+    }
+    a0 = n0;
+    a1 = n1;
+  }
+  float* out = part + (size_t)blockIdx.y * T * EP;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = wv * 32 + m * 16 + (lane >> 4) * 4 + r;
+      if (t < T) {
+#pragma unroll
+        for (int n = 0; n < NF; ++n) out[(size_t)t * EP + n * 16 + (lane & 15)] = acc[m][n][r];
+      }
+    }
+}
+
 // one wave per token: z = sum of the d-slice partials in order, then route_token
 template <int EPL>
 __global__ __launch_bounds__(256) void topk_kernel(RouteLaunch a) {
@@ -480,6 +595,22 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteLaunch a) {
 
 template <int EP>
 moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
+  const int kslice = a.d / a.split;
+  const size_t fused_lds = (size_t)(kslice / 32) * 3 * EP * 64;
+  if (a.T <= 256 && fused_lds <= kFusedRouterLds && (size_t)kslice * EP <= 16384) {
+    // more than 64 KB of dynamic LDS needs the attribute (set on the current device)
+    if (hipFuncSetAttribute((const void*)router_fused_kernel<EP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kFusedRouterLds) != hipSuccess)
+      return fail(MOE_ERR_HIP, "hipFuncSetAttribute(router_fused_kernel) failed");
+    int tok = begin_launch("router_mfma", s);
+    hipLaunchKernelGGL(router_fused_kernel<EP>, dim3(1, a.split), dim3(512), fused_lds, s, (const uint16_t*)a.x,
+                       a.w_router, a.part, a.T, a.d, a.E, kslice);
+    moe_status st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+    tok = begin_launch("route_topk", s);
+    hipLaunchKernelGGL(topk_kernel<(EP + 63) / 64>, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+    return end_launch(tok, s);
+  }
   int tok = begin_launch("router_prep", s);
   hipLaunchKernelGGL(router_prep_kernel, dim3(a.d / 64, (unsigned)ceil_div(EP, 64)), dim3(256), 0, s,
                      a.w_router, a.wt, a.d, a.E, EP);
@@ -536,9 +667,9 @@ void route_plan(int T, int d, int E, int act_dtype, int* ep, int* split) {
   const int tblocks = (int)ceil_div(std::max(T, 1), 256);
   const int target = std::max(1, device_cu_count() / tblocks);
   const int steps = d / 32;
-  // at least eight 32-wide steps per slice: for few tokens the grid stays small
+  // at least four 32-wide steps per slice: for few tokens the grid stays small
   // and the top-k pass has few partials to add
-  int sp = std::min(target, std::max(1, steps / 8));
+  int sp = std::min(target, std::max(1, steps / 4));
   while (steps % sp) --sp;
   *split = sp;
 }
