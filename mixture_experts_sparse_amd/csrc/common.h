@@ -120,6 +120,8 @@ struct PermuteLaunch {
   int64_t rows;          // permuted rows provided by the caller
   int fb = 0;            // fallback experts per token after the top-k (topk_idx has k + fb columns)
   int32_t* reroute = nullptr;  // workspace [2 T k + E + 1] for re-routing (fb > 0 with a limit)
+  int32_t* tiles = nullptr;  // or: also write the grouped GEMM's tile lists for tile height
+  int tile_bm = 0;           // tile_bm (layout of GemmLaunch::tile_prefix; not with re-routing)
 };
 moe_status launch_permute(const PermuteLaunch& a, hipStream_t s);
 

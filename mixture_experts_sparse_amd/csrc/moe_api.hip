@@ -285,15 +285,20 @@ moe_status run_route(const moe_config* c, const void* x, const float* w_router, 
   return launch_route(r, s);
 }
 
+// tiles / tile_bm: also write the routed gate/up GEMM's tile lists (moe_forward),
+// which the permute does unless overflow re-routing moves rows after its scan
 moe_status run_permute(const moe_config* c, const void* x, const int32_t* topk_idx, int32_t* counts,
                        int32_t* offsets, int32_t* dest_row, int32_t* src_token, int32_t* n_dropped,
-                       void* x_perm, int32_t* stats, char* ws, hipStream_t s) {
+                       void* x_perm, int32_t* stats, char* ws, hipStream_t s, int32_t* tiles = nullptr,
+                       int tile_bm = 0) {
   const Layout L = layout_of(c);
   PermuteLaunch p{x, topk_idx, counts, offsets, dest_row, src_token, n_dropped, x_perm, stats,
                   (int32_t*)(ws + L.hist), c->T, c->d, c->E, c->top_k, dtype_bytes(c->act_dtype),
                   capacity_of(c), perm_rows(c)};
   p.fb = c->reroute_depth;
   p.reroute = (int32_t*)(ws + L.reroute);
+  p.tiles = tiles;
+  p.tile_bm = tile_bm;
   return launch_permute(p, s);
 }
 
@@ -313,14 +318,16 @@ GemmLaunch gate_up_launch(const moe_config* c, const void* x, const void* x_perm
 // reduce_partials: fold the down pass's K-split partial sums into y_perm / y_shared
 // (the standalone entry point); moe_forward leaves them for the combine to add.
 // gather: src_token when the gate/up pass reads x directly (x_perm is then unused).
+// tiles_ready: the permute already wrote the gate/up pass's tile lists
 moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const int32_t* gather,
                    const int32_t* offsets, const moe_expert_weights* w, float* y_perm, float* y_shared, char* ws,
-                   bool reduce_partials, hipStream_t s) {
+                   bool reduce_partials, hipStream_t s, bool tiles_ready = false) {
   if (c->T == 0) return MOE_OK;
   const Layout L = layout_of(c);
   const int64_t R = perm_rows(c);
   // routed experts: gate/up pass then down pass
   GemmLaunch g = gate_up_launch(c, x, x_perm, gather, offsets, w, ws);
+  g.tiles_ready = tiles_ready;
   moe_status st = launch_grouped_gemm(g, s);
   if (st != MOE_OK) return st;
   const int bm_gate_up = grouped_gemm_bm(g);
@@ -509,10 +516,16 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
   if (st != MOE_OK) return st;
   // gather fusion: when the gate/up kernel can read the token rows through
   // src_token, the permute writes no x_perm and the rows are read once, by the GEMM
-  const bool gather = cfg->T > 0 && gather_ok(gate_up_launch(cfg, x, x_perm, src, offsets, weights, w), cfg->T);
-  st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, gather ? nullptr : x_perm, stats, w, s);
+  const GemmLaunch gu = gate_up_launch(cfg, x, x_perm, src, offsets, weights, w);
+  const bool gather = cfg->T > 0 && gather_ok(gu, cfg->T);
+  // the permute's scan block also writes the gate/up tile lists, unless
+  // re-routing moves rows after it
+  const bool tiles_in_permute = cfg->T > 0 && !(cfg->reroute_depth > 0 && capacity_of(cfg) >= 0);
+  st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, gather ? nullptr : x_perm, stats, w, s,
+                   tiles_in_permute ? (int32_t*)(w + layout_of(cfg).tiles) : nullptr, grouped_gemm_bm(gu));
   if (st != MOE_OK) return st;
-  st = run_ffn(cfg, x, x_perm, gather ? src : nullptr, offsets, weights, y_perm, y_sh, w, false, s);
+  st = run_ffn(cfg, x, x_perm, gather ? src : nullptr, offsets, weights, y_perm, y_sh, w, false, s,
+               tiles_in_permute);
   if (st != MOE_OK) return st;
   return run_combine(cfg, y_perm, y_sh, dest, tw, out, w, s);
 }

@@ -29,6 +29,35 @@ __device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, int 
   return idx[(size_t)(p / k) * ld + (p % k)];
 }
 
+// The grouped GEMM's tile lists (the layout tiles_kernel writes: offsets,
+// exclusive prefix of m-tiles per expert, the expert of every m-tile) from the
+// final per-expert row counts, by the one block that knows them.  Thread e holds
+// expert e's kept rows and exclusive row offset; `scan` is 256 ints of LDS.
+__device__ __forceinline__ void write_tile_lists(int e, int kept, int off_excl, int E, int bm, int* scan,
+                                                 int32_t* __restrict__ tiles) {
+  const int nt = (e < E) ? (kept + bm - 1) / bm : 0;
+  scan[e] = nt;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive sum scan
+    const int v = (e >= off) ? scan[e - off] : 0;
+    __syncthreads();
+    scan[e] += v;
+    __syncthreads();
+  }
+  int32_t* goff = tiles;
+  int32_t* tp = tiles + E + 1;
+  int32_t* tile_group = tiles + 2 * (E + 1);
+  if (e < E) {
+    goff[e] = off_excl;
+    tp[e] = scan[e] - nt;
+    for (int m = scan[e] - nt; m < scan[e]; ++m) tile_group[m] = e;
+  }
+  if (e == E - 1) {
+    goff[E] = off_excl + kept;
+    tp[E] = scan[e];
+  }
+}
+
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx,
                                                         int32_t* __restrict__ hist, int P, int E, int k,
                                                         int ld) {
@@ -51,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(int32_t* __restrict__ hi
                                                         int64_t cap, int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ n_dropped,
-                                                        int32_t* __restrict__ stats) {
+                                                        int32_t* __restrict__ stats,
+                                                        int32_t* __restrict__ tiles, int tile_bm) {
   __shared__ int kept_s[256];
   __shared__ int drop_s[256];
   const int e = threadIdx.x;
@@ -85,6 +115,11 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(int32_t* __restrict__ hi
     offsets[0] = 0;
     n_dropped[0] = drop_s[255];
     if (stats) stats[2 * E] = drop_s[255];
+  }
+  if (tiles) {
+    const int incl = kept_s[e];
+    __syncthreads();  // (kept_s is reused as the tile scan)
+    write_tile_lists(e, kept, incl - kept, E, tile_bm, kept_s, tiles);
   }
 }
 
@@ -169,7 +204,8 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __r
                                                               int32_t* __restrict__ n_dropped,
                                                               int32_t* __restrict__ stats,
                                                               int32_t* __restrict__ dest_row,
-                                                              int32_t* __restrict__ src_token) {
+                                                              int32_t* __restrict__ src_token,
+                                                              int32_t* __restrict__ tiles, int tile_bm) {
   __shared__ int running[256];
   __shared__ int wcnt[4][256];
   __shared__ int kept_s[256];
@@ -210,6 +246,8 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __r
     n_dropped[0] = drop_s[255];
     if (stats) stats[2 * E] = drop_s[255];
   }
+  __syncthreads();
+  if (tiles) write_tile_lists(e, kept, kept_s[e] - kept, E, tile_bm, drop_s, tiles);
   running[e] = 0;  // ranks start at zero in the only chunk
   __syncthreads();
   const int n_rows = off_s[E];
@@ -449,12 +487,15 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
     return end_launch(tok, s);
   }
   const int ld = a.k + a.fb;
+  // tile lists for the GEMM when the first pass's rows are final (no re-routing)
+  int32_t* tiles = (a.tiles && a.tile_bm > 0 && !(a.fb > 0 && a.capacity >= 0)) ? a.tiles : nullptr;
   int tok;
   moe_status st;
   if (nblk == 1) {
     tok = begin_launch("permute_count_rank", s);
     hipLaunchKernelGGL(count_rank_kernel, dim3(1), dim3(kThreads), 0, s, a.topk_idx, P, a.E, a.k, ld, a.capacity,
-                       a.rows, a.counts, a.offsets, a.n_dropped, a.stats, a.dest_row, a.src_token);
+                       a.rows, a.counts, a.offsets, a.n_dropped, a.stats, a.dest_row, a.src_token, tiles,
+                       a.tile_bm);
     st = end_launch(tok, s);
     if (st != MOE_OK) return st;
   } else {
@@ -465,7 +506,7 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
 
     tok = begin_launch("permute_scan", s);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, s, a.hist, nblk, a.E, a.capacity,
-                       a.counts, a.offsets, a.n_dropped, a.stats);
+                       a.counts, a.offsets, a.n_dropped, a.stats, tiles, a.tile_bm);
     st = end_launch(tok, s);
     if (st != MOE_OK) return st;
 
