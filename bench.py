@@ -128,6 +128,13 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
     }
     # load balancing (--balance): the logits (and Gumbel uniforms) read once
     work["balance_stats"] = {"bytes": T * E * 4 * (2 if sh.gumbel else 1)}
+    # one-chunk count/scan/rank: the pair ids in, dest_row and src_token out
+    work["permute_count_rank"] = {"bytes": T * k * 8 + N * 4}
+    # overflow re-routing: each token's k + D expert ids and its k first-pass rows
+    # in, a fallback expert and rank per pair out; relocation: the same pairs again
+    D = sh.reroute_depth
+    work["permute_reroute"] = {"bytes": T * (k + D) * 4 + T * k * 4 + 2 * T * k * 4}
+    work["permute_relocate"] = {"bytes": T * k * 4 * 4 + N * 4}
     if sh.n_shared:
         work["shared_gate_up"] = {"flop": 4.0 * T * d * F, "bytes": T * d * a + 2 * F * d * wb + sc_gu + T * F * hb}
         work["shared_down"] = {"flop": 2.0 * T * F * d, "bytes": T * F * hb + d * F * wb + sc_dn + T * d * 4}
