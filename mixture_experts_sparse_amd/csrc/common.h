@@ -174,6 +174,7 @@ struct GemmLaunch {
   bool shared;              // the shared expert (names its launches apart)
   const int32_t* gather = nullptr;  // row r of A is A[gather[r]] (A = x, gather = src_token), or
                                     // null for a dense A; only kernels that gather_ok() admits
+  int64_t group_rows_max = -1;  // most rows any group can hold (the capacity), or -1: unknown
   bool tiles_ready = false; // tile_prefix already holds this launch's tile lists (same
                             // offsets, groups, max_rows and tile height as a previous launch)
   int split_k = 1;          // down pass: K split into parts; part 0 goes to `out`,

@@ -41,8 +41,6 @@ constexpr int kKS = 128;                // k per step
 constexpr int kBM = 16;                 // rows per tile
 constexpr int kNF = 4;                  // 16-row weight fragments per tile
 constexpr int kAROW = kKS * 2;          // bytes of one activation row per step
-constexpr int kASTAGE = kBM * kAROW;    // 4 KB
-constexpr int kAINS = kASTAGE / 1024;   // 1 KB direct-to-LDS loads per wave per step
 
 constexpr unsigned vmcnt_imm(int n) { return 0x0F70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
 constexpr unsigned kLgkm0 = 0xC07Fu;  // lgkmcnt(0) alone
@@ -63,10 +61,17 @@ __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 #ifndef KS_PD_INT4
 #define KS_PD_INT4 4
 #endif
+// with at most 4 rows per expert (capacity 1-4: decode) only those rows are staged
+#ifndef KS_PD4_FP8
+#define KS_PD4_FP8 3
+#endif
+#ifndef KS_PD4_INT4
+#define KS_PD4_INT4 4
+#endif
 
 enum { WT_BF16 = 0, WT_FP8 = 1, WT_INT4 = 2 };
 
-template <int WT>
+template <int WT, int AR>
 struct Codec {
   static constexpr int RAW = WT == WT_BF16 ? 4 : WT == WT_FP8 ? 2 : 1;  // 16-byte loads per fragment per step
   static constexpr int NQ = WT == WT_INT4 ? 1 : 0;                       // group words per fragment per step
@@ -74,7 +79,9 @@ struct Codec {
   // prefetch distance D in steps, for the weights (registers) and the activations
   // (D + 1 LDS stages per wave) alike: the waits count loads in issue order, so
   // the weights are only ever as far ahead as the activations issued beside them
-  static constexpr int PD = WT == WT_BF16 ? KS_PD_BF16 : WT == WT_FP8 ? KS_PD_FP8 : KS_PD_INT4;
+  static constexpr int PD = WT == WT_BF16 ? KS_PD_BF16
+                            : WT == WT_FP8  ? (AR == 4 ? KS_PD4_FP8 : KS_PD_FP8)
+                                            : (AR == 4 ? KS_PD4_INT4 : KS_PD_INT4);
   static constexpr int NB = kNF * (RAW + NQ);                            // weight loads per wave per step
 };
 
@@ -93,13 +100,13 @@ struct KsplitParams {
 
 template <int WT>
 struct WSet {
-  uint4 w[kNF][Codec<WT>::RAW];
-  uint32_t q[kNF][Codec<WT>::NQ > 0 ? Codec<WT>::NQ : 1];
+  uint4 w[kNF][Codec<WT, 16>::RAW];
+  uint32_t q[kNF][Codec<WT, 16>::NQ > 0 ? Codec<WT, 16>::NQ : 1];
 };
 
 // 8 bf16 of sub-step s from a lane's raw weight registers of one fragment
 template <int WT>
-__device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Codec<WT>::RAW], int s) {
+__device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Codec<WT, 16>::RAW], int s) {
   if constexpr (WT == WT_BF16) {
     return __builtin_bit_cast(bf16x8_t, raw[s]);
   } else if constexpr (WT == WT_FP8) {
@@ -117,13 +124,19 @@ __device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Codec<WT>::RAW], i
   }
 }
 
-template <bool GATED, int WT>
+// AR: activation rows staged per tile, 16 (every tile) or 4 (tiles of at most 4
+// rows: fragment row r reads staged row r & 3, so rows 4-15 of the MFMA repeat
+// rows 0-3 and are never stored)
+template <bool GATED, int WT, int AR>
 __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p) {
-  using CD = Codec<WT>;
+  using CD = Codec<WT, AR>;
   constexpr int PD = CD::PD, R = PD + 1, NB = CD::NB;
   constexpr int NST = PD + 1;  // activation stages per wave
+  constexpr int kASTAGE = AR * kAROW;   // bytes per stage
+  constexpr int kAINS = kASTAGE / 1024; // 1 KB direct-to-LDS loads per wave per step
   static_assert(PD >= 2 && (PD - 1) * (NB + kAINS) <= 63, "vmcnt holds at most 63 loads");
   static_assert(4 * NST * kASTAGE * KS_OCC <= 160 * 1024, "LDS of the resident blocks");
+  static_assert(4 * NST * kASTAGE >= 4 * kNF * 4 * 64 * 4, "the partial sums meet in the stage memory");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * NST * kASTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -141,7 +154,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
   const size_t RB = (size_t)K * CD::STEP_BYTES / kKS;  // bytes per weight row
   const size_t KG = (size_t)K / kKS;                    // group words per weight row
   uint8_t* As = smem + w * (NST * kASTAGE);
-  const uint32_t afrag = (uint32_t)(r16 * kAROW);
+  const uint32_t afrag = (uint32_t)((r16 % AR) * kAROW);
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
@@ -187,23 +200,29 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
         b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * (CD::STEP_BYTES / 4);
         q_row[j] = (const uint32_t*)qbase + row * KG;
       }
+      // Steps past this wave's last (prefetches near the end) still issue their
+      // loads -- the waits count them -- but every lane reads one common address,
+      // so each such instruction costs one request and no bandwidth.
       auto issue_a = [&](int k) {  // k: local step
         uint8_t* st = As + (k % NST) * kASTAGE;
+        const bool live = k < nk;
         const uint32_t kb = (uint32_t)(k0 + min(k, nk - 1)) * kAROW;
 #pragma unroll
         for (int i = 0; i < kAINS; ++i)
-          __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[i] + kb), MOE_LPTR(st + i * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(MOE_GPTR(live ? a_base + a_off[i] + kb : (const uint8_t*)p.A),
+                                           MOE_LPTR(st + i * 1024), 16, 0, 0);
       };
       auto load_w = [&](WSet<WT>& d, int k) {
+        const bool live = k < nk;
         const int kc = k0 + min(k, nk - 1);
 #pragma unroll
         for (int j = 0; j < kNF; ++j)
 #pragma unroll
           for (int u = 0; u < CD::RAW; ++u)
-            d.w[j][u] = *(const uint4*)(b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 16);
+            d.w[j][u] = *(const uint4*)(live ? b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 16 : (const uint8_t*)p.B0);
         if constexpr (CD::NQ > 0) {
 #pragma unroll
-          for (int j = 0; j < kNF; ++j) d.q[j][0] = q_row[j][kc];
+          for (int j = 0; j < kNF; ++j) d.q[j][0] = live ? q_row[j][kc] : *(const uint32_t*)p.S0;
         }
       };
 
@@ -227,7 +246,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
         f32x4_t t[kNF], rs = zero4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ r16) * 16);
+          const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ (r16 % AR)) * 16);
           const bf16x8_t af = *(const bf16x8_t*)(st + afrag + slot);
           bf16x8_t bf[kNF];
 #pragma unroll
@@ -333,6 +352,8 @@ moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const in
   grid = ceil_div(grid, 8) * 8;  // the XCD mapping wants a multiple of 8
   if (grid <= 0) return MOE_OK;
   const int wt = a.w_dtype == MOE_FP8_E4M3FN ? WT_FP8 : a.w_dtype == MOE_INT4 ? WT_INT4 : WT_BF16;
+  // every group has at most 4 rows (capacity 1-4): stage only those
+  const bool few = a.group_rows_max >= 0 && a.group_rows_max <= 4 && wt != WT_BF16;
   static const char* const kNames[2][2][3] = {
       {{"gemm_down_bf16", "gemm_down_fp8", "gemm_down_int4"},
        {"gemm_gate_up_bf16", "gemm_gate_up_fp8", "gemm_gate_up_int4"}},
@@ -340,14 +361,25 @@ moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const in
        {"shared_gate_up_bf16", "shared_gate_up_fp8", "shared_gate_up_int4"}}};
   int tok = begin_launch(kNames[a.shared][a.gated][wt], s);
   const dim3 gd((unsigned)grid), bd(256);
+  auto go = [&](auto gated, auto wtag, auto ar) {
+    hipLaunchKernelGGL((gemm_ksplit_kernel<decltype(gated)::value, decltype(wtag)::value, decltype(ar)::value>), gd,
+                       bd, 0, s, p);
+  };
+  using T1 = std::true_type;
+  using F1 = std::false_type;
+  using B = std::integral_constant<int, WT_BF16>;
+  using F8 = std::integral_constant<int, WT_FP8>;
+  using I4 = std::integral_constant<int, WT_INT4>;
+  using A16 = std::integral_constant<int, 16>;
+  using A4 = std::integral_constant<int, 4>;
   if (a.gated) {
-    if (wt == WT_BF16) hipLaunchKernelGGL((gemm_ksplit_kernel<true, WT_BF16>), gd, bd, 0, s, p);
-    else if (wt == WT_FP8) hipLaunchKernelGGL((gemm_ksplit_kernel<true, WT_FP8>), gd, bd, 0, s, p);
-    else hipLaunchKernelGGL((gemm_ksplit_kernel<true, WT_INT4>), gd, bd, 0, s, p);
+    if (wt == WT_BF16) go(T1{}, B{}, A16{});
+    else if (wt == WT_FP8) { if (few) go(T1{}, F8{}, A4{}); else go(T1{}, F8{}, A16{}); }
+    else { if (few) go(T1{}, I4{}, A4{}); else go(T1{}, I4{}, A16{}); }
   } else {
-    if (wt == WT_BF16) hipLaunchKernelGGL((gemm_ksplit_kernel<false, WT_BF16>), gd, bd, 0, s, p);
-    else if (wt == WT_FP8) hipLaunchKernelGGL((gemm_ksplit_kernel<false, WT_FP8>), gd, bd, 0, s, p);
-    else hipLaunchKernelGGL((gemm_ksplit_kernel<false, WT_INT4>), gd, bd, 0, s, p);
+    if (wt == WT_BF16) go(F1{}, B{}, A16{});
+    else if (wt == WT_FP8) { if (few) go(F1{}, F8{}, A4{}); else go(F1{}, F8{}, A16{}); }
+    else { if (few) go(F1{}, I4{}, A4{}); else go(F1{}, I4{}, A16{}); }
   }
   return end_launch(tok, s);
 }

@@ -312,6 +312,8 @@ GemmLaunch gate_up_launch(const moe_config* c, const void* x, const void* x_perm
   g.B0 = w->w_gate; g.B1 = w->w_up; g.S0 = w->s_gate; g.S1 = w->s_up;
   g.out = ws + L.h; g.offsets = offsets; g.tile_prefix = (int32_t*)(ws + L.tiles);
   g.groups = c->E; g.single_rows = 0; g.max_rows = perm_rows(c); g.K = c->d; g.N = c->F; g.gated = true;
+  // with re-routing a group still holds at most C rows
+  g.group_rows_max = capacity_of(c) >= 0 ? std::min<int64_t>(capacity_of(c), g.max_rows) : g.max_rows;
   return g;
 }
 
@@ -344,7 +346,7 @@ moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const
   g.A = x; g.B0 = w->sh_gate; g.B1 = w->sh_up; g.S0 = w->sh_s_gate; g.S1 = w->sh_s_up;
   g.out = ws + L.h_sh; g.offsets = nullptr; g.tile_prefix = (int32_t*)(ws + L.tiles_sh);
   g.groups = 1; g.single_rows = c->T; g.max_rows = c->T; g.K = c->d; g.N = c->F; g.gated = true;
-  g.shared = true; g.tiles_ready = false; g.split_k = 1;
+  g.shared = true; g.tiles_ready = false; g.split_k = 1; g.group_rows_max = c->T;
   st = launch_grouped_gemm(g, s);
   if (st != MOE_OK) return st;
   const int bm_sh = grouped_gemm_bm(g);

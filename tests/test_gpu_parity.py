@@ -63,6 +63,10 @@ SMALL = {
     "int4_small": W.shrink(WK["skewed_int4_decode"], T=300, d=256, F=256),
     "int4_rows": WK["mixtral_bf16"].replace(name="i4r", T=500, d=256, E=8, k=2, F=384, w_dtype=W.DT_INT4),
     "int4_shared": W.shrink(WK["fine_shared_bf16"], T=150, d=256, F=128).replace(w_dtype=W.DT_INT4),
+    # capacity 3 and 4 (at most 4 rows per expert): the decode GEMM stages only 4
+    # activation rows; groups of 2-4 rows exercise the row aliasing
+    "fp8_cap3": W.shrink(WK["skewed_fp8"], T=200, d=256, F=256),
+    "int4_cap4": W.shrink(WK["skewed_int4_decode"], T=230, d=512, F=384),
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
