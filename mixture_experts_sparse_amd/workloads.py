@@ -199,12 +199,23 @@ def _expert_tensor(shape: MoEShape, name: str, n_exp: int, rows: int, cols: int,
         scales = torch.empty((n_exp, rows, cols // INT4_GROUP), dtype=torch.int32, device=device)
     else:
         scales = None
-    for e in range(n_exp):
-        w32 = _normal((rows, cols), 0.02, child_seed(shape.seed, name, e), device)
+    # experts are drawn one by one (one seed each) into a float32 chunk of at
+    # most ~1 GiB, which is scaled and stored in one go: every step is
+    # elementwise or reduces within a row, so the result does not depend on
+    # the chunking, and far fewer small launches are made than expert by expert
+    chunk = max(1, min(n_exp, (1 << 30) // max(1, rows * cols * 4)))
+    for e0 in range(0, n_exp, chunk):
+        n = min(chunk, n_exp - e0)
+        w32 = torch.empty((n, rows, cols), dtype=torch.float32, device=device)
+        for i in range(n):
+            g = torch.Generator(device=device)
+            g.manual_seed(child_seed(shape.seed, name, e0 + i))
+            torch.randn((rows, cols), generator=g, out=w32[i])
+        w32.mul_(0.02)
         w, s = _store_weight(w32, w_dtype)
-        out[e].copy_(w)
+        out[e0:e0 + n].copy_(w)
         if scales is not None:
-            scales[e].copy_(s)
+            scales[e0:e0 + n].copy_(s)
         del w32, w
     return out, scales
 
