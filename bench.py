@@ -131,9 +131,13 @@ def algorithmic_work(sh, kept_rows: int, touched: int):
     # one-chunk count/scan/rank: the pair ids in, dest_row and src_token out
     work["permute_count_rank"] = {"bytes": T * k * 8 + N * 4}
     # overflow re-routing: each token's k + D expert ids and its k first-pass rows
-    # in, a fallback expert and rank per pair out; relocation: the same pairs again
+    # in, a state word per token out (init); per round the same in, a fallback
+    # expert and rank per pair out; the finish kernel sums E counts per block of
+    # proposals and writes the offsets; relocation: the pairs again
     D = sh.reroute_depth
-    work["permute_reroute"] = {"bytes": T * (k + D) * 4 + T * k * 4 + 2 * T * k * 4}
+    work["permute_reroute_init"] = {"bytes": T * (k + D) * 4 + T * k * 4 + T * 4}
+    work["permute_reroute_round"] = {"bytes": T * (k + D) * 4 + T * k * 4 + 2 * T * 4 + 2 * T * k * 4}
+    work["permute_reroute_finish"] = {"bytes": -(-T // 256) * E * 4 + 3 * (E + 1) * 4}
     work["permute_relocate"] = {"bytes": T * k * 4 * 4 + N * 4}
     if sh.n_shared:
         work["shared_gate_up"] = {"flop": 4.0 * T * d * F, "bytes": T * d * a + 2 * F * d * wb + sc_gu + T * F * hb}

@@ -109,6 +109,20 @@ void route_plan(int T, int d, int E, int act_dtype, int* ep, int* split);
 
 // Permutation geometry: pairs are processed in chunks of kPermChunk.
 constexpr int kPermChunk = 1024;
+// Overflow re-routing runs in rounds over blocks of kRerouteTokens tokens; at
+// most reroute_rounds(D) rounds before the exact one-wave walk takes over.
+constexpr int kRerouteTokens = 256;
+inline int reroute_rounds(int D) { return 2 * D + 2; }
+// per-block proposal counts are kept expert-major, each expert's row padded to
+// a multiple of 4 blocks (16-byte loads)
+__host__ __device__ inline int reroute_count_ld(int nb) { return (nb + 3) & ~3; }
+// int32 workspace of re-routing: per-block proposal counts (two rounds), the
+// re-routed expert and rank per pair, the first pass's offsets, per-token
+// state, and one "something was rejected" flag per round
+inline int64_t reroute_ws_ints(int64_t T, int k, int E, int D) {
+  const int nb = (int)((T + kRerouteTokens - 1) / kRerouteTokens);
+  return 2 * (int64_t)reroute_count_ld(nb) * E + 2 * T * k + (E + 1) + T + reroute_rounds(D);
+}
 struct PermuteLaunch {
   const void* x; const int32_t* topk_idx;
   int32_t* counts; int32_t* offsets; int32_t* dest_row; int32_t* src_token; int32_t* n_dropped;
@@ -119,7 +133,7 @@ struct PermuteLaunch {
   int64_t capacity;      // < 0: no limit
   int64_t rows;          // permuted rows provided by the caller
   int fb = 0;            // fallback experts per token after the top-k (topk_idx has k + fb columns)
-  int32_t* reroute = nullptr;  // workspace [2 T k + E + 1] for re-routing (fb > 0 with a limit)
+  int32_t* reroute = nullptr;  // workspace of reroute_ws_ints(T, k, E, fb) (fb > 0 with a limit)
   int32_t* tiles = nullptr;  // or: also write the grouped GEMM's tile lists for tile height
   int tile_bm = 0;           // tile_bm (layout of GemmLaunch::tile_prefix; not with re-routing)
 };

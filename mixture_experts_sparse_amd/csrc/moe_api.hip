@@ -194,7 +194,7 @@ Layout layout_of(const moe_config* c) {
   // scratch shared by moe_permute and moe_expert_ffn (they never run concurrently
   // on one workspace within moe_forward; standalone callers pass one each)
   L.hist = take(sizeof(int32_t) * nblk * c->E);
-  L.reroute = take(c->reroute_depth > 0 ? sizeof(int32_t) * (2 * (size_t)P + c->E + 1) : 0);
+  L.reroute = take(c->reroute_depth > 0 ? sizeof(int32_t) * reroute_ws_ints(c->T, c->top_k, c->E, c->reroute_depth) : 0);
   L.perm_end = o;
   L.tiles = take(sizeof(int32_t) * tile_list_ints(c->E, R));
   L.tiles_sh = take(sizeof(int32_t) * tile_list_ints(1, c->T));

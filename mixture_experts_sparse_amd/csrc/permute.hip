@@ -258,19 +258,218 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __r
 
 // Overflow re-routing (page "Parameter scale and the truth about sparse
 // activation" (deepseek.csdn.net), s3.2 level 2: an overflowed token goes to
-// its next-best expert that is not full).  The serial rule -- dropped pairs in
-// (t, j) order, each taking the first of its token's D fallback experts that is
-// below capacity and not already serving the token -- is computed by one wave
-// over chunks of whole tokens in order.  Inside a chunk the lanes settle by
-// deferred acceptance: every unsettled lane proposes its next fallback, a lane
-// loses an expert to an earlier lane of its own token, or when its rank among
-// the lanes holding that expert reaches the expert's remaining room, and losers
-// propose again until no lane loses.  All experts rank lanes in the same (t, j)
-// order, so this reaches exactly the serial assignment; the chunk's winners then
-// use up their experts' room before the next chunk starts.
+// its next-best expert that is not full).  The rule is serial: the dropped
+// pairs in (t, j) order, each taking the first of its token's D fallback
+// experts that is below capacity and not already serving the token.
+//
+// Two facts make it parallel.  (1) Within a token, the overflowed slots simply
+// take the first m available experts of the list in list order (slot order
+// follows list order): an entry skipped by one slot stays unavailable for the
+// next.  (2) Every expert ranks the tokens the same way, (t) order; then
+// deferred acceptance -- every token proposes to its first m entries not yet
+// rejected, each expert holds the proposals ranked below its remaining room and
+// rejects the rest, rejected tokens propose again -- ends in exactly the serial
+// assignment (with one common priority order the stable assignment is unique
+// and is the serial one).  A proposal's rank at expert c is the number of
+// earlier tokens proposing c: the proposal counts of the blocks before mine
+// plus a popcount over a per-expert bitmap of my block's proposers.
+//
+// Kernels: rr_init_kernel (per token: overflowed slots m, entries that can never
+// be taken -- ids outside [0,E), experts already full after the first pass,
+// repeats of an earlier entry -- and the first proposals' per-block counts),
+// then up to reroute_rounds(D) launches of rr_round_kernel (a round that follows
+// one without rejections returns at once), then reroute_kernel: if some round
+// rejected nothing, the last round's ranks are final and it only books the
+// rows; otherwise the one-wave walk below computes the assignment itself.
 //   out: re_e[p] (fallback expert or -1), re_rank[p] (rank among the expert's
 //   re-routed pairs), off_first (the first pass's offsets), offsets (final),
 //   stats kept / n_dropped (final)
+
+// a token's state word: bits 0-7 entries rejected (or never available), bits
+// 8-15 overflowed slots m
+__device__ __forceinline__ int rr_props(int rej, int m) {
+  int pm = 0, got = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const bool take = got < m && !((rej >> i) & 1);
+    pm |= take ? (1 << i) : 0;
+    got += take ? 1 : 0;
+  }
+  return pm;
+}
+
+__device__ __forceinline__ void rr_list(const int32_t* __restrict__ idx, int ld, int k, int D, int t, int (&f)[8]) {
+  const int32_t* row = idx + (size_t)t * ld + k;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = i < D ? row[i] : -1;
+}
+
+__device__ __forceinline__ bool rr_over(const int32_t* __restrict__ idx, const int32_t* __restrict__ dest_row,
+                                        int ld, int k, int E, int t, int j) {
+  const int e = idx[(size_t)t * ld + j];
+  return e >= 0 && e < E && dest_row[(size_t)t * k + j] < 0;
+}
+
+// out[e] = sum of cnt[e * ld + b] over blocks b < nbk, for every expert e < E
+// (per-block proposal counts are stored expert-major, ld a multiple of 4 and
+// cnt 16-byte aligned).  Thread e reads its expert's run with 16-byte loads,
+// 64 blocks' counts in flight at once: the counts were written by the previous
+// launch, possibly through another XCD's L2, so each round trip is long.
+__device__ __forceinline__ void rr_expert_sums(const int32_t* __restrict__ cnt, int ld, int nbk, int E, int* out) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const int4* row = reinterpret_cast<const int4*>(cnt + (size_t)e * ld);
+  int sum = 0;
+  for (int b0 = 0; b0 < nbk; b0 += 64) {
+    int4 v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = (b0 + 4 * u < nbk) ? row[b0 / 4 + u] : make_int4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int b = b0 + 4 * u;
+      sum += (b < nbk ? v[u].x : 0) + (b + 1 < nbk ? v[u].y : 0) + (b + 2 < nbk ? v[u].z : 0) +
+             (b + 3 < nbk ? v[u].w : 0);
+    }
+  }
+  out[e] = sum;
+}
+
+__global__ __launch_bounds__(kRerouteTokens) void rr_init_kernel(const int32_t* __restrict__ idx, int ld, int k,
+                                                                 int D, int T, int E, int cap,
+                                                                 const int32_t* __restrict__ counts,
+                                                                 const int32_t* __restrict__ dest_row,
+                                                                 int32_t* __restrict__ state,
+                                                                 int32_t* __restrict__ cnt0,
+                                                                 int32_t* __restrict__ changed, int R) {
+  __shared__ int room[256];
+  __shared__ int tot[256];
+  const int tid = threadIdx.x;
+  room[tid] = tid < E ? cap - min(counts[tid], cap) : 0;
+  tot[tid] = 0;
+  if (blockIdx.x == 0 && tid < R) changed[tid] = 0;
+  __syncthreads();
+  const int t = blockIdx.x * kRerouteTokens + tid;
+  if (t < T) {
+    int m = 0;
+    for (int j = 0; j < k; ++j) m += rr_over(idx, dest_row, ld, k, E, t, j) ? 1 : 0;
+    int f[8];
+    rr_list(idx, ld, k, D, t, f);
+    int rej = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = f[i];
+      bool never = i >= D || c < 0 || c >= E;
+      if (!never) never = room[c] <= 0;
+#pragma unroll
+      for (int i2 = 0; i2 < i; ++i2) never = never || f[i2] == c;
+      rej |= never ? (1 << i) : 0;
+    }
+    state[t] = rej | (m << 8);
+    const int pm = m > 0 ? rr_props(rej, m) : 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      if ((pm >> i) & 1) atomicAdd(&tot[f[i]], 1);
+  }
+  __syncthreads();
+  if (tid < E) cnt0[(size_t)tid * reroute_count_ld(gridDim.x) + blockIdx.x] = tot[tid];
+}
+
+// One round of deferred acceptance over every token.  cur: the per-block
+// counts of this round's proposals (written by the previous launch); nxt: the
+// counts of the next round's.  Every overflowed slot's re_e / re_rank is
+// written from this round's proposals: after a round without rejections they
+// are final.
+__global__ __launch_bounds__(kRerouteTokens) void rr_round_kernel(const int32_t* __restrict__ idx, int ld, int k,
+                                                                  int D, int T, int E, int cap,
+                                                                  const int32_t* __restrict__ counts,
+                                                                  const int32_t* __restrict__ dest_row,
+                                                                  int32_t* __restrict__ state,
+                                                                  const int32_t* __restrict__ cur,
+                                                                  int32_t* __restrict__ nxt,
+                                                                  int32_t* __restrict__ changed, int r,
+                                                                  int32_t* __restrict__ re_e,
+                                                                  int32_t* __restrict__ re_rank) {
+  if (r > 0 && changed[r - 1] == 0) return;  // an earlier round settled every token
+  constexpr int kWords = kRerouteTokens / 32;
+  __shared__ int room[256];
+  __shared__ int pre[256];
+  __shared__ int tot[256];
+  __shared__ uint32_t bits[256 * kWords];  // bit (c, tok): my block's token tok proposes c
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;
+  room[tid] = tid < E ? cap - min(counts[tid], cap) : 0;
+  tot[tid] = 0;
+  rr_expert_sums(cur, reroute_count_ld(gridDim.x), b, E, pre);  // proposals of the blocks before mine
+  for (int w = tid; w < E * kWords; w += kRerouteTokens) bits[w] = 0;
+  __syncthreads();
+  const int t = b * kRerouteTokens + tid;
+  const int st = t < T ? state[t] : 0;
+  int rej = st & 0xFF;
+  const int m = st >> 8;
+  int f[8];
+  int pm = 0;
+  if (m > 0) {
+    rr_list(idx, ld, k, D, t, f);
+    pm = rr_props(rej, m);
+  }
+  const int word = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((pm >> i) & 1) atomicOr(&bits[f[i] * kWords + word], 1u << (tid & 31));
+  __syncthreads();
+  int g[8];
+  bool lost = false;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    g[i] = 0;
+    if ((pm >> i) & 1) {
+      const int c = f[i];
+      const uint32_t* row = bits + c * kWords;
+      int rk = pre[c];
+      for (int q = 0; q < word; ++q) rk += __popc(row[q]);
+      rk += __popc(row[word] & below);
+      g[i] = rk;
+      if (rk >= room[c]) {
+        rej |= 1 << i;
+        lost = true;
+      }
+    }
+  }
+  if (m > 0) {
+    // the a-th overflowed slot (j order) takes the a-th proposal (list order)
+    int j = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if ((pm >> i) & 1) {
+        while (j < k && !rr_over(idx, dest_row, ld, k, E, t, j)) ++j;
+        if (j < k) {
+          re_e[(size_t)t * k + j] = f[i];
+          re_rank[(size_t)t * k + j] = g[i];
+          ++j;
+        }
+      }
+    }
+    for (; j < k; ++j)
+      if (rr_over(idx, dest_row, ld, k, E, t, j)) re_e[(size_t)t * k + j] = -1;
+  }
+  if (lost) {
+    state[t] = rej | (m << 8);
+    pm = rr_props(rej, m);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    if ((pm >> i) & 1) atomicAdd(&tot[f[i]], 1);
+  const int any_lost = __syncthreads_or(lost ? 1 : 0);
+  if (tid < E) nxt[(size_t)tid * reroute_count_ld(gridDim.x) + b] = tot[tid];
+  if (tid == 0 && any_lost) atomicOr(&changed[r], 1);
+}
+
+// The exact walk for inputs that the rounds did not settle: one wave over
+// chunks of whole tokens in order, the lanes of a chunk settling among
+// themselves by the same deferred acceptance (a lane also loses an expert to
+// an earlier lane of its own token); the chunk's winners then use up their
+// experts' room before the next chunk starts.
 // A chunk's inputs, loaded one chunk ahead so the sequential walk never waits
 // on memory: the pair's routed expert, its first-pass row and its token's D
 // fallback experts (ids outside [0,E) from a caller count as no candidate).
@@ -307,18 +506,22 @@ __device__ __forceinline__ void advance(RerouteLane& v) {
 
 __global__ __launch_bounds__(64) void reroute_kernel(const int32_t* __restrict__ idx, int ld, int k, int D,
                                                      int T, int E, int cap, const int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ offsets, int32_t* __restrict__ off_first,
                                                      const int32_t* __restrict__ dest_row,
                                                      int32_t* __restrict__ re_e, int32_t* __restrict__ re_rank,
-                                                     int32_t* __restrict__ n_dropped, int32_t* __restrict__ stats) {
+                                                     const int32_t* __restrict__ changed, int R,
+                                                     int32_t* __restrict__ cnt, int nb) {
   __shared__ int room[256];
   __shared__ int given[256];
   const int lane = threadIdx.x;
+  // nothing to do when the rounds settled: some round rejected nothing (the
+  // flags of the rounds after it stay zero too)
+  bool settled_lane = false;
+  for (int r = lane; r < R; r += 64) settled_lane = settled_lane || changed[r] == 0;
+  if (__ballot(settled_lane) != 0) return;
   for (int e = lane; e < 256; e += 64) {
     room[e] = e < E ? cap - min(counts[e], cap) : 0;
     given[e] = 0;
   }
-  for (int e = lane; e <= E; e += 64) off_first[e] = offsets[e];
   __syncthreads();
   const int tpc = 64 / k;      // whole tokens per chunk
   const int lanes = tpc * k;
@@ -388,21 +591,51 @@ __global__ __launch_bounds__(64) void reroute_kernel(const int32_t* __restrict__
     }
     __syncthreads();
   }
-  // final rows per expert, their exclusive scan, and the pairs left dropped
-  __shared__ int kept_f[256];
-  for (int e = lane; e < 256; e += 64) kept_f[e] = e < E ? min(counts[e], cap) + given[e] : 0;
+  // the rows given to each expert, where rr_finish_kernel sums them (the first
+  // block's column of the per-block counts, the other columns zero)
+  for (int e = lane; e < E; e += 64)
+    for (int b = 0; b < nb; ++b) cnt[(size_t)e * reroute_count_ld(nb) + b] = b == 0 ? given[e] : 0;
+}
+
+// Books the rows: kept = the first pass's rows + the re-routed pairs given to
+// each expert, their exclusive scan (the final offsets; the first pass's are
+// kept for the relocation), the pairs left dropped and the kept statistics.
+__global__ __launch_bounds__(256) void rr_finish_kernel(int E, int cap, const int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ off_first,
+                                                        const int32_t* __restrict__ cnt, int nb,
+                                                        int32_t* __restrict__ n_dropped,
+                                                        int32_t* __restrict__ stats) {
+  __shared__ int given[256];
+  __shared__ int kept_s[256];
+  __shared__ int req_s[256];
+  const int e = threadIdx.x;
+  rr_expert_sums(cnt, reroute_count_ld(nb), nb, E, given);
+  const int first = e < E ? offsets[e] : 0;
+  const int first_end = e == 0 ? offsets[E] : 0;
   __syncthreads();
-  if (lane == 0) {
-    int run = 0, req = 0;
-    for (int e = 0; e < E; ++e) {
-      offsets[e] = run;
-      run += kept_f[e];
-      req += counts[e];
-      if (stats) stats[E + e] = kept_f[e];
-    }
-    offsets[E] = run;
-    n_dropped[0] = req - run;
-    if (stats) stats[2 * E] = req - run;
+  const int kept = e < E ? min(counts[e], cap) + given[e] : 0;
+  kept_s[e] = kept;
+  req_s[e] = e < E ? counts[e] : 0;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {  // inclusive sum scans
+    const int v = e >= off ? kept_s[e - off] : 0;
+    const int q = e >= off ? req_s[e - off] : 0;
+    __syncthreads();
+    kept_s[e] += v;
+    req_s[e] += q;
+    __syncthreads();
+  }
+  if (e < E) off_first[e] = first;
+  if (e == 0) off_first[E] = first_end;
+  if (e < E) {
+    offsets[e] = kept_s[e] - kept;
+    if (stats) stats[E + e] = kept;
+  }
+  if (e == 255) {
+    offsets[E] = kept_s[255];
+    n_dropped[0] = req_s[255] - kept_s[255];
+    if (stats) stats[2 * E] = req_s[255] - kept_s[255];
   }
 }
 
@@ -518,13 +751,37 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
   }
 
   if (a.fb > 0 && a.capacity >= 0) {
-    int32_t* re_e = a.reroute;
+    const int nb = (int)ceil_div(a.T, kRerouteTokens);
+    const size_t cnt_ints = (size_t)reroute_count_ld(nb) * a.E;  // one round's counts
+    int32_t* cnt = a.reroute;  // 16-byte aligned: first in the workspace
+    int32_t* re_e = cnt + 2 * cnt_ints;
     int32_t* re_rank = re_e + P;
     int32_t* off_first = re_rank + P;
-    tok = begin_launch("permute_reroute", s);
-    hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(64), 0, s, a.topk_idx, ld, a.k, a.fb, a.T, a.E,
-                       (int)a.capacity, a.counts, a.offsets, off_first, a.dest_row, re_e, re_rank, a.n_dropped,
-                       a.stats);
+    int32_t* state = off_first + a.E + 1;
+    int32_t* changed = state + a.T;
+    const int R = reroute_rounds(a.fb);
+    const int cap = (int)a.capacity;
+    tok = begin_launch("permute_reroute_init", s);
+    hipLaunchKernelGGL(rr_init_kernel, dim3(nb), dim3(kRerouteTokens), 0, s, a.topk_idx, ld, a.k, a.fb, a.T, a.E,
+                       cap, a.counts, a.dest_row, state, cnt, changed, R);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+    for (int r = 0; r < R; ++r) {
+      tok = begin_launch("permute_reroute_round", s);
+      hipLaunchKernelGGL(rr_round_kernel, dim3(nb), dim3(kRerouteTokens), 0, s, a.topk_idx, ld, a.k, a.fb, a.T,
+                         a.E, cap, a.counts, a.dest_row, state, cnt + (r & 1) * cnt_ints,
+                         cnt + ((r + 1) & 1) * cnt_ints, changed, r, re_e, re_rank);
+      st = end_launch(tok, s);
+      if (st != MOE_OK) return st;
+    }
+    tok = begin_launch("permute_reroute_walk", s);
+    hipLaunchKernelGGL(reroute_kernel, dim3(1), dim3(64), 0, s, a.topk_idx, ld, a.k, a.fb, a.T, a.E, cap,
+                       a.counts, a.dest_row, re_e, re_rank, changed, R, cnt, nb);
+    st = end_launch(tok, s);
+    if (st != MOE_OK) return st;
+    tok = begin_launch("permute_reroute_finish", s);
+    hipLaunchKernelGGL(rr_finish_kernel, dim3(1), dim3(256), 0, s, a.E, cap, a.counts, a.offsets, off_first, cnt, nb,
+                       a.n_dropped, a.stats);
     st = end_launch(tok, s);
     if (st != MOE_OK) return st;
     tok = begin_launch("permute_relocate", s);

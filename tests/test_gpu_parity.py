@@ -219,3 +219,79 @@ def test_permute_ignores_out_of_range_ids(dev):
     assert int(counts.sum()) == sh.T * sh.k - 2
     assert int(dest[3, 0]) == -1 and int(dest[10, 1]) == -1
     assert int(offsets[-1]) == sh.T * sh.k - 2
+
+
+def _permute_direct(sh: W.MoEShape, idx: np.ndarray, dev):
+    """moe_permute on caller-made indices (top-k then fallback columns)."""
+    lib = G.L()
+    cfg = lib.make_config(sh)
+    T, k = sh.T, sh.k
+    x = torch.randn((T, sh.d), device=dev).to(torch.bfloat16)
+    idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(dev)
+    R = lib.permuted_rows(cfg)
+    counts = torch.empty(sh.E, dtype=torch.int32, device=dev)
+    offsets = torch.empty(sh.E + 1, dtype=torch.int32, device=dev)
+    dest = torch.empty((T, k), dtype=torch.int32, device=dev)
+    src = torch.empty(max(R, 1), dtype=torch.int32, device=dev)
+    nd = torch.empty(1, dtype=torch.int32, device=dev)
+    xp = torch.empty((max(R, 1), sh.d), dtype=torch.bfloat16, device=dev)
+    ws = lib.alloc_workspace(cfg, dev)
+    lib.moe_permute(cfg, x, idx_t, counts, offsets, dest, src, nd, xp, ws)
+    torch.cuda.synchronize()
+    return {"counts": G.to_np(counts), "offsets": G.to_np(offsets), "dest_row": G.to_np(dest),
+            "src_token": G.to_np(src)[:R], "n_dropped": int(nd.item())}
+
+
+def _check_reroute(sh, idx, dev):
+    g = _permute_direct(sh, idx, dev)
+    P = O.permute_reroute(idx[:, : sh.k], idx[:, sh.k:], sh.E, G.oracle_capacity(sh))
+    assert np.array_equal(g["counts"], P.counts)
+    assert np.array_equal(g["offsets"], P.offsets)
+    assert np.array_equal(g["dest_row"], P.dest_row)
+    assert g["n_dropped"] == P.n_dropped
+    n = int(P.offsets[-1])
+    assert np.array_equal(g["src_token"][:n], P.src_token[:n])
+    return P
+
+
+@pytest.mark.parametrize("T,E,k,D,cf,dup", [(5000, 64, 2, 4, 1.0, False), (3001, 128, 2, 4, 1.25, False),
+                                            (2500, 32, 4, 8, 0.8, False), (1800, 64, 8, 3, 1.0, False),
+                                            (4000, 64, 2, 6, 1.0, True), (257, 16, 3, 2, 0.5, True)])
+def test_reroute_many_blocks_matches_oracle(T, E, k, D, cf, dup, dev):
+    """Re-routing over several 256-token blocks: skewed expert picks (each
+    token's top-k and fallbacks distinct, drawn with weights ~ u^3), or lists
+    with repeated fallback entries, bit-exact against the oracle's serial rule."""
+    rng = np.random.default_rng(T * 7 + E + k + D)
+    p = rng.random(E) ** 3
+    p /= p.sum()
+    idx = np.stack([rng.choice(E, size=k + D, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    if dup:
+        m = rng.random((T, D)) < 0.15
+        idx[:, k:][m] = rng.integers(0, E, size=int(m.sum()))
+    sh = WK["mixtral_bf16"].replace(name="rrdirect", T=T, d=128, E=E, k=k, F=128, capacity_factor=cf,
+                                    reroute_depth=D)
+    P = _check_reroute(sh, idx, dev)
+    assert P.n_dropped < int(np.sum(np.maximum(P.counts - G.oracle_capacity(sh), 0)))  # some pairs moved
+
+
+@pytest.mark.parametrize("n", [4, 12])
+def test_reroute_displacement_chain(n, dev):
+    """A chain where each re-routed token displaces the next one from its first
+    fallback: token 1 takes A1, token i >= 2 lists (A_{i-1}, A_i) and ends on A_i.
+    Settling it by rounds of proposals takes n rounds (one displacement each):
+    n = 4 fits the round limit for D = 2, n = 12 exceeds it and the exact
+    one-wave walk decides; the tokens of the chain sit in different 256-token
+    blocks."""
+    T, E, k, D = 1400, 16, 1, 2
+    sh = WK["mixtral_bf16"].replace(name="rrchain", T=T, d=128, E=E, k=k, F=128, capacity_factor=0.02,
+                                    reroute_depth=D)
+    assert G.oracle_capacity(sh) == 1
+    Z, X = 0, 15
+    idx = np.full((T, k + D), Z, dtype=np.int32)  # fillers: every entry the full expert Z
+    pos = [100 * i + 37 for i in range(1, n + 1)]
+    for i, t in enumerate(pos, start=1):
+        idx[t] = [Z, i, X] if i == 1 else [Z, i - 1, i]
+    P = _check_reroute(sh, idx, dev)
+    for i, t in enumerate(pos, start=1):  # token i ends on expert i
+        row = P.dest_row[t, 0]
+        assert P.offsets[i] <= row < P.offsets[i + 1]
