@@ -342,6 +342,245 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
   }
 }
 
+// Tiles of at most 4 rows with K split evenly, INT4 weights (decode): the
+// tile work of gemm_ksplit_kernel<GATED, WT_INT4, 4>, but each wave's load
+// stream runs on across the block's tiles.  A wave's steps over its tiles form
+// one sequence, and PD steps ahead of the step it computes it requests the
+// weights and activations of the step PD later -- in the next tile once this
+// one has no more -- so the prefetch never drains at a tile boundary; the
+// partial sums meet in an LDS area of their own while the next tile's loads
+// are in flight.  Needs K / 128 = 4 nk steps with nk a multiple of PD + 1 (a
+// step's ring slot and LDS stage are then the same in every tile).  Every
+// vector load of the stream is one the waits count: the tile table and the
+// gathered token indices come through scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* cint_ptr;
+
+// A block barrier after this wave's LDS operations have completed -- and
+// nothing else: __syncthreads would also wait for every load in flight, which
+// here are the next tile's prefetches.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkm0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __forceinline__ TileRef map_tile_scalar(int L, int n_tiles, int groups, int bm, cint_ptr tp,
+                                                   cint_ptr goff) {
+  L = __builtin_amdgcn_readfirstlane(L);
+  const int g = tp[groups + 1 + L / n_tiles];
+  const int mt = tp[g + 1] - tp[g];
+  const int local = L - tp[g] * n_tiles;
+  TileRef r;
+  r.g = g;
+  r.nt = local / mt;
+  r.row0 = goff[g] + (local % mt) * bm;
+  r.rows = min(bm, goff[g + 1] - r.row0);
+  return r;
+}
+
+template <bool GATED, int PD>
+__global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitParams p) {
+  constexpr int WT = WT_INT4, AR = 4;
+  using CD = Codec<WT, AR>;
+  constexpr int R = PD + 1;
+  constexpr int NS = kNF + 1;   // loads of a step: one 16-byte weight load per fragment + the activations
+  constexpr int NQ = kNF;       // + at a chunk's first step: one group-word load per fragment
+  constexpr int kASTAGE = AR * kAROW;        // 1 KB: one direct-to-LDS load per step
+  constexpr int kRED = 4 * kNF * 4 * 64 * 4;  // the four waves' partial sums
+  static_assert(kASTAGE == 1024, "one activation load per step");
+  static_assert(R <= 4, "a chunk's group words: one per lane group");
+  static_assert(PD >= 2 && (PD - 1) * NS + NQ <= 63, "vmcnt holds at most 63 loads");
+  static_assert(KS_OCC * (4 * R * kASTAGE + kRED) <= 160 * 1024, "LDS of the resident blocks");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * R * kASTAGE + kRED];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = p.K, N = p.N;
+  const int nk = K / kKS / 4;  // steps per wave per tile (the host checks 4 nk = K / 128, nk % R == 0)
+  const int k0 = w * nk;
+  cint_ptr tp = (cint_ptr)p.tp;
+  cint_ptr goff = (cint_ptr)p.goff;
+  cint_ptr gat = (cint_ptr)p.gather;
+  const int total = p.n_tiles * tp[p.groups];
+  const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
+  const int chunk = (total + 7) >> 3;
+  const int lend = min(total, (xcd + 1) * chunk);
+  const int L0 = xcd * chunk + jb;
+  if (L0 >= lend) return;  // the whole block: no tile
+  const int n_units = (lend - L0 + G8 - 1) / G8;
+  const int g4 = lane >> 4, r16 = lane & 15;
+  const size_t RB = (size_t)K * CD::STEP_BYTES / kKS;
+  const size_t KG = (size_t)K / kKS;
+  uint8_t* As = smem + w * (R * kASTAGE);
+  float* red = (float*)(smem + 4 * R * kASTAGE);  // [wave][fragment][r][lane]
+  const uint32_t afrag = (uint32_t)((r16 & 3) * kAROW);
+  const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
+  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
+
+  // ---- the issue side: the tile whose steps are being requested (past the
+  // block's last tile every lane reads one common address: one request each)
+  const uint8_t* a_src;
+  const uint8_t* b_row[kNF];
+  const uint32_t* q_row[kNF];
+  bool ilive;
+  auto set_issue = [&](int iu) {
+    ilive = iu < n_units;
+    const TileRef tr = map_tile_scalar(L0 + min(iu, n_units - 1) * G8, p.n_tiles, p.groups, kBM, tp, goff);
+    // activations: lane -> row lane / 16 (rows past the group's end repeat its
+    // last row), 16-byte chunk slot lane % 16 <- chunk slot ^ row
+    const int r = lane >> 4;
+    const int c = (lane & 15) ^ r;
+    uint32_t src;
+    if (p.gather) {
+      const int s0 = gat[tr.row0];
+      const int s1 = gat[tr.row0 + min(1, tr.rows - 1)];
+      const int s2 = gat[tr.row0 + min(2, tr.rows - 1)];
+      const int s3 = gat[tr.row0 + min(3, tr.rows - 1)];
+      src = (uint32_t)(r == 0 ? s0 : r == 1 ? s1 : r == 2 ? s2 : s3);
+    } else {
+      src = (uint32_t)(tr.row0 + min(r, tr.rows - 1));
+    }
+    a_src = (const uint8_t*)p.A + (size_t)src * K * 2 + c * 16;
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) {
+      int wrow;
+      const void* base;
+      const void* qbase;
+      if (GATED) {  // fragments 0,1: gate rows; 2,3: the matching up rows
+        wrow = tr.nt * 32 + (j & 1) * 16 + r16;
+        base = (j < 2) ? p.B0 : p.B1;
+        qbase = (j < 2) ? p.S0 : p.S1;
+      } else {
+        wrow = tr.nt * 64 + j * 16 + r16;
+        base = p.B0;
+        qbase = p.S0;
+      }
+      const size_t row = (size_t)tr.g * N + wrow;
+      b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * (CD::STEP_BYTES / 4);
+      q_row[j] = (const uint32_t*)qbase + row * KG;
+    }
+  };
+  // one step's loads, into ring slot / LDS stage `slot`: the weights of local
+  // step k of the issue tile; at a chunk's first step the chunk's group words,
+  // spread over the lanes (lane group g4 < R: the word of step k + g4 of its
+  // fragment row) -- one load per fragment per chunk instead of one per step;
+  // then the activations
+  uint4 wr[R][kNF][1];
+  uint32_t qd[kNF];
+  auto issue = [&](int slot, int k, auto chunk_start) {
+    const int kc = k0 + k;
+#pragma unroll
+    for (int j = 0; j < kNF; ++j)
+      wr[slot][j][0] = *(const uint4*)(ilive ? b_row[j] + (size_t)kc * CD::STEP_BYTES : (const uint8_t*)p.B0);
+    if constexpr (decltype(chunk_start)::value) {
+#pragma unroll
+      for (int j = 0; j < kNF; ++j) qd[j] = ilive ? q_row[j][kc + min(g4, R - 1)] : *(const uint32_t*)p.S0;
+    }
+    issue_fence();
+    __builtin_amdgcn_global_load_lds(MOE_GPTR(ilive ? a_src + (size_t)kc * kAROW : (const uint8_t*)p.A),
+                                     MOE_LPTR(As + slot * kASTAGE), 16, 0, 0);
+    issue_fence();
+  };
+
+  set_issue(0);
+  issue(0, 0, std::true_type{});
+#pragma unroll
+  for (int u = 1; u < PD; ++u) issue(u, u, std::false_type{});
+
+  for (int cu = 0; cu < n_units; ++cu) {
+    const TileRef tr = map_tile_scalar(L0 + cu * G8, p.n_tiles, p.groups, kBM, tp, goff);
+    f32x4_t acc[kNF];
+#pragma unroll
+    for (int j = 0; j < kNF; ++j) acc[j] = zero4;
+    for (int kb = 0; kb < nk; kb += R) {
+      uint32_t qw[R][kNF];  // this chunk's group word of each step and fragment
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int k = kb + u;
+        // landed: all but the loads of the PD - 1 steps requested after this one
+        // (one of them a chunk's first step, with its group words, unless this
+        // step or the one before starts a chunk); epilogue stores between them
+        // only make the wait stricter
+        if (u >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm((PD - 1) * NS + NQ));
+        else __builtin_amdgcn_s_waitcnt(vmcnt_imm((PD - 1) * NS));
+        // this wave's reads of the previous step are done before its stage is refilled
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (u == 0) {
+          // the chunk's words (landed with its first step) to every lane of a row;
+          // qd is then free for the next chunk's, requested below at u == 1
+#pragma unroll
+          for (int v = 0; v < R; ++v)
+#pragma unroll
+            for (int j = 0; j < kNF; ++j) qw[v][j] = (uint32_t)__shfl((int)qd[j], v * 16 + r16);
+        }
+        if (u == 1 && kb + R == nk) set_issue(cu + 1);  // k + PD == nk: the next tile's steps from here
+        const int kn = k + PD < nk ? k + PD : k + PD - nk;
+        // (u + PD) % R == 0 exactly when u == 1: the requested step starts a chunk
+        if (u == 1) issue((u + PD) % R, kn, std::true_type{});
+        else issue((u + PD) % R, kn, std::false_type{});
+        const uint8_t* st = As + u * kASTAGE;
+        f32x4_t t[kNF], rs = zero4;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ (r16 & 3)) * 16);
+          const bf16x8_t af = *(const bf16x8_t*)(st + afrag + slot);
+          rs = mfma16x16x32(af, ones, s == 0 ? zero4 : rs);
+#pragma unroll
+          for (int j = 0; j < kNF; ++j) t[j] = mfma16x16x32(af, b_frag<WT>(wr[u][j], s), s == 0 ? zero4 : t[j]);
+        }
+#pragma unroll
+        for (int j = 0; j < kNF; ++j) {
+          const uint32_t q = qw[u][j];
+          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(q & 0xFFFFu));
+          const float c = (float)(128u + ((q >> 16) & 15u));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc, fmaf(-c, rs[r], t[j][r]), acc[j][r]);
+        }
+      }
+    }
+
+    // ---- the four partial sums meet in their own LDS area (the stages hold the
+    // next tile's loads in flight); fixed order wave 0 + 1 + 2 + 3
+#pragma unroll
+    for (int j = 0; j < kNF; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) red[((w * kNF + j) * 4 + r) * 64 + lane] = acc[j][r];
+    lds_barrier();
+    auto total_of = [&](int j, int r) {
+      float v = red[((0 * kNF + j) * 4 + r) * 64 + lane];
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) v += red[((ww * kNF + j) * 4 + r) * 64 + lane];
+      return v;
+    };
+    const int rq = g4 * 4;
+    if (GATED) {
+      if (w < 2) {
+        const int j = w;
+        const int f = tr.nt * 32 + j * 16 + r16;
+        uint16_t* h = (uint16_t*)p.out;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = rq + r;
+          if (m < tr.rows) h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(total_of(j, r)) * total_of(j + 2, r));
+        }
+      }
+    } else {
+      const int j = w;
+      const int n = tr.nt * 64 + j * 16 + r16;
+      float* y = (float*)p.out;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = rq + r;
+        if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = total_of(j, r);
+      }
+    }
+    lds_barrier();  // the partial sums are read before the next tile writes them
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
+}
+
 }  // namespace
 
 moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s) {
@@ -361,6 +600,19 @@ moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const in
        {"shared_gate_up_bf16", "shared_gate_up_fp8", "shared_gate_up_int4"}}};
   int tok = begin_launch(kNames[a.shared][a.gated][wt], s);
   const dim3 gd((unsigned)grid), bd(256);
+  // INT4 tiles of at most 4 rows, K split evenly: the load stream runs across tiles
+  const int ksteps = a.K / kKS;
+  const int nk = ksteps / 4;
+  if (few && wt == WT_INT4 && ksteps % 4 == 0 && nk > 0 && (nk % 4 == 0 || nk % 3 == 0)) {
+    if (nk % 4 == 0) {
+      if (a.gated) hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<true, 3>), gd, bd, 0, s, p);
+      else hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<false, 3>), gd, bd, 0, s, p);
+    } else {
+      if (a.gated) hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<true, 2>), gd, bd, 0, s, p);
+      else hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<false, 2>), gd, bd, 0, s, p);
+    }
+    return end_launch(tok, s);
+  }
   auto go = [&](auto gated, auto wtag, auto ar) {
     hipLaunchKernelGGL((gemm_ksplit_kernel<decltype(gated)::value, decltype(wtag)::value, decltype(ar)::value>), gd,
                        bd, 0, s, p);
