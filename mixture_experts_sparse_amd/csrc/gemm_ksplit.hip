@@ -379,15 +379,18 @@ __device__ __forceinline__ TileRef map_tile_scalar(int L, int n_tiles, int group
   return r;
 }
 
-template <bool GATED, int PD>
+template <bool GATED, int WT, int PD>
 __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitParams p) {
-  constexpr int WT = WT_INT4, AR = 4;
+  static_assert(WT == WT_INT4 || WT == WT_FP8, "INT4 or fp8 weights");
+  constexpr int AR = 4;
   using CD = Codec<WT, AR>;
   constexpr int R = PD + 1;
-  constexpr int NS = kNF + 1;   // loads of a step: one 16-byte weight load per fragment + the activations
-  constexpr int NQ = kNF;       // + at a chunk's first step: one group-word load per fragment
-  constexpr int kASTAGE = AR * kAROW;        // 1 KB: one direct-to-LDS load per step
-  constexpr int kRED = 4 * kNF * 4 * 64 * 4;  // the four waves' partial sums
+  constexpr int NS = kNF * CD::RAW + 1;            // loads of a step: 16-byte weight loads + the activations
+  // + at a chunk's first step: INT4, one group-word load per fragment; fp8, the
+  // row scales of the tile (read for real only when the chunk starts a tile)
+  constexpr int NQ = WT == WT_INT4 ? kNF : (GATED ? 2 : 1);
+  constexpr int kASTAGE = AR * kAROW;              // 1 KB: one direct-to-LDS load per step
+  constexpr int kRED = 4 * kNF * 4 * 64 * 4;       // the four waves' partial sums
   static_assert(kASTAGE == 1024, "one activation load per step");
   static_assert(R <= 4, "a chunk's group words: one per lane group");
   static_assert(PD >= 2 && (PD - 1) * NS + NQ <= 63, "vmcnt holds at most 63 loads");
@@ -423,6 +426,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
   const uint8_t* a_src;
   const uint8_t* b_row[kNF];
   const uint32_t* q_row[kNF];
+  const float* sc_at[2];  // fp8: where this lane's output-row scales of the tile are
   bool ilive;
   auto set_issue = [&](int iu) {
     ilive = iu < n_units;
@@ -460,22 +464,40 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
       b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * (CD::STEP_BYTES / 4);
       q_row[j] = (const uint32_t*)qbase + row * KG;
     }
+    if constexpr (WT == WT_FP8) {
+      // the epilogue's rows: gated, wave w < 2 writes h column nt 32 + 16 w + r16
+      // (gate and up scale); otherwise wave w writes y column nt 64 + 16 w + r16
+      const int col = GATED ? tr.nt * 32 + (w & 1) * 16 + r16 : tr.nt * 64 + w * 16 + r16;
+      sc_at[0] = (const float*)p.S0 + (size_t)tr.g * N + col;
+      sc_at[1] = GATED ? (const float*)p.S1 + (size_t)tr.g * N + col : sc_at[0];
+    }
   };
   // one step's loads, into ring slot / LDS stage `slot`: the weights of local
-  // step k of the issue tile; at a chunk's first step the chunk's group words,
-  // spread over the lanes (lane group g4 < R: the word of step k + g4 of its
-  // fragment row) -- one load per fragment per chunk instead of one per step;
-  // then the activations
-  uint4 wr[R][kNF][1];
+  // step k of the issue tile; at a chunk's first step, INT4: the chunk's group
+  // words spread over the lanes (lane group g4 < R: the word of step k + g4 of
+  // its fragment row) -- one load per fragment per chunk instead of one per
+  // step; fp8: the tile's row scales when the chunk starts the tile, else a
+  // load of the common address (no branch: the waits stay exact); then the
+  // activations
+  uint4 wr[R][kNF][CD::RAW];
   uint32_t qd[kNF];
+  float sl[2];
   auto issue = [&](int slot, int k, auto chunk_start) {
     const int kc = k0 + k;
 #pragma unroll
     for (int j = 0; j < kNF; ++j)
-      wr[slot][j][0] = *(const uint4*)(ilive ? b_row[j] + (size_t)kc * CD::STEP_BYTES : (const uint8_t*)p.B0);
-    if constexpr (decltype(chunk_start)::value) {
 #pragma unroll
-      for (int j = 0; j < kNF; ++j) qd[j] = ilive ? q_row[j][kc + min(g4, R - 1)] : *(const uint32_t*)p.S0;
+      for (int u = 0; u < CD::RAW; ++u)
+        wr[slot][j][u] =
+            *(const uint4*)(ilive ? b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 16 : (const uint8_t*)p.B0);
+    if constexpr (decltype(chunk_start)::value) {
+      if constexpr (WT == WT_INT4) {
+#pragma unroll
+        for (int j = 0; j < kNF; ++j) qd[j] = ilive ? q_row[j][kc + min(g4, R - 1)] : *(const uint32_t*)p.S0;
+      } else {
+#pragma unroll
+        for (int i = 0; i < NQ; ++i) sl[i] = *(ilive && k == 0 ? sc_at[i] : (const float*)p.S0);
+      }
     }
     issue_fence();
     __builtin_amdgcn_global_load_lds(MOE_GPTR(ilive ? a_src + (size_t)kc * kAROW : (const uint8_t*)p.A),
@@ -488,18 +510,19 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
 #pragma unroll
   for (int u = 1; u < PD; ++u) issue(u, u, std::false_type{});
 
+  float st_sc[2] = {1.f, 1.f};  // fp8: the current tile's row scales
   for (int cu = 0; cu < n_units; ++cu) {
     const TileRef tr = map_tile_scalar(L0 + cu * G8, p.n_tiles, p.groups, kBM, tp, goff);
     f32x4_t acc[kNF];
 #pragma unroll
     for (int j = 0; j < kNF; ++j) acc[j] = zero4;
     for (int kb = 0; kb < nk; kb += R) {
-      uint32_t qw[R][kNF];  // this chunk's group word of each step and fragment
+      uint32_t qw[R][kNF];  // INT4: this chunk's group word of each step and fragment
 #pragma unroll
       for (int u = 0; u < R; ++u) {
         const int k = kb + u;
         // landed: all but the loads of the PD - 1 steps requested after this one
-        // (one of them a chunk's first step, with its group words, unless this
+        // (one of them a chunk's first step, with its extra loads, unless this
         // step or the one before starts a chunk); epilogue stores between them
         // only make the wait stricter
         if (u >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm((PD - 1) * NS + NQ));
@@ -508,12 +531,18 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
         __builtin_amdgcn_s_waitcnt(kLgkm0);
         __builtin_amdgcn_sched_barrier(0);
         if (u == 0) {
-          // the chunk's words (landed with its first step) to every lane of a row;
-          // qd is then free for the next chunk's, requested below at u == 1
+          // what landed with the chunk's first step: INT4, the chunk's words to every
+          // lane of a row (qd is then free for the next chunk's, requested at u == 1);
+          // fp8, in the tile's first chunk, the tile's scales (likewise)
+          if constexpr (WT == WT_INT4) {
 #pragma unroll
-          for (int v = 0; v < R; ++v)
+            for (int v = 0; v < R; ++v)
 #pragma unroll
-            for (int j = 0; j < kNF; ++j) qw[v][j] = (uint32_t)__shfl((int)qd[j], v * 16 + r16);
+              for (int j = 0; j < kNF; ++j) qw[v][j] = (uint32_t)__shfl((int)qd[j], v * 16 + r16);
+          } else {
+#pragma unroll
+            for (int i = 0; i < NQ; ++i) st_sc[i] = kb == 0 ? sl[i] : st_sc[i];
+          }
         }
         if (u == 1 && kb + R == nk) set_issue(cu + 1);  // k + PD == nk: the next tile's steps from here
         const int kn = k + PD < nk ? k + PD : k + PD - nk;
@@ -526,17 +555,24 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
         for (int s = 0; s < 4; ++s) {
           const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ (r16 & 3)) * 16);
           const bf16x8_t af = *(const bf16x8_t*)(st + afrag + slot);
-          rs = mfma16x16x32(af, ones, s == 0 ? zero4 : rs);
+          if constexpr (WT == WT_INT4) {
+            rs = mfma16x16x32(af, ones, s == 0 ? zero4 : rs);
 #pragma unroll
-          for (int j = 0; j < kNF; ++j) t[j] = mfma16x16x32(af, b_frag<WT>(wr[u][j], s), s == 0 ? zero4 : t[j]);
+            for (int j = 0; j < kNF; ++j) t[j] = mfma16x16x32(af, b_frag<WT>(wr[u][j], s), s == 0 ? zero4 : t[j]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < kNF; ++j) acc[j] = mfma16x16x32(af, b_frag<WT>(wr[u][j], s), acc[j]);
+          }
         }
+        if constexpr (WT == WT_INT4) {
 #pragma unroll
-        for (int j = 0; j < kNF; ++j) {
-          const uint32_t q = qw[u][j];
-          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(q & 0xFFFFu));
-          const float c = (float)(128u + ((q >> 16) & 15u));
+          for (int j = 0; j < kNF; ++j) {
+            const uint32_t q = qw[u][j];
+            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(q & 0xFFFFu));
+            const float c = (float)(128u + ((q >> 16) & 15u));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc, fmaf(-c, rs[r], t[j][r]), acc[j][r]);
+            for (int r = 0; r < 4; ++r) acc[j][r] = fmaf(sc, fmaf(-c, rs[r], t[j][r]), acc[j][r]);
+          }
         }
       }
     }
@@ -563,7 +599,9 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int m = rq + r;
-          if (m < tr.rows) h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(total_of(j, r)) * total_of(j + 2, r));
+          if (m < tr.rows)
+            h[(size_t)(tr.row0 + m) * N + f] =
+                f32_to_bf16_rne(silu_f32(total_of(j, r) * st_sc[0]) * (total_of(j + 2, r) * st_sc[1]));
         }
       }
     } else {
@@ -573,7 +611,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = rq + r;
-        if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = total_of(j, r);
+        if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = total_of(j, r) * st_sc[0];
       }
     }
     lds_barrier();  // the partial sums are read before the next tile writes them
@@ -600,17 +638,20 @@ moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const in
        {"shared_gate_up_bf16", "shared_gate_up_fp8", "shared_gate_up_int4"}}};
   int tok = begin_launch(kNames[a.shared][a.gated][wt], s);
   const dim3 gd((unsigned)grid), bd(256);
-  // INT4 tiles of at most 4 rows, K split evenly: the load stream runs across tiles
+  // INT4 or fp8 tiles of at most 4 rows, K split evenly: the load stream runs across tiles
   const int ksteps = a.K / kKS;
   const int nk = ksteps / 4;
-  if (few && wt == WT_INT4 && ksteps % 4 == 0 && nk > 0 && (nk % 4 == 0 || nk % 3 == 0)) {
-    if (nk % 4 == 0) {
-      if (a.gated) hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<true, 3>), gd, bd, 0, s, p);
-      else hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<false, 3>), gd, bd, 0, s, p);
-    } else {
-      if (a.gated) hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<true, 2>), gd, bd, 0, s, p);
-      else hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<false, 2>), gd, bd, 0, s, p);
-    }
+  if (few && ksteps % 4 == 0 && nk > 0 && (nk % 4 == 0 || nk % 3 == 0)) {
+    auto pipe = [&](auto gated, auto wtag) {
+      constexpr bool G = decltype(gated)::value;
+      constexpr int WTv = decltype(wtag)::value;
+      if (nk % 4 == 0) hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<G, WTv, 3>), gd, bd, 0, s, p);
+      else hipLaunchKernelGGL((gemm_ksplit_pipe_kernel<G, WTv, 2>), gd, bd, 0, s, p);
+    };
+    using I4p = std::integral_constant<int, WT_INT4>;
+    using F8p = std::integral_constant<int, WT_FP8>;
+    if (a.gated) { if (wt == WT_INT4) pipe(std::true_type{}, I4p{}); else pipe(std::true_type{}, F8p{}); }
+    else { if (wt == WT_INT4) pipe(std::false_type{}, I4p{}); else pipe(std::false_type{}, F8p{}); }
     return end_launch(tok, s);
   }
   auto go = [&](auto gated, auto wtag, auto ar) {

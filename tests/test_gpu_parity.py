@@ -67,11 +67,13 @@ SMALL = {
     # activation rows; groups of 2-4 rows exercise the row aliasing
     "fp8_cap3": W.shrink(WK["skewed_fp8"], T=200, d=256, F=256),
     "int4_cap4": W.shrink(WK["skewed_int4_decode"], T=230, d=512, F=384),
-    # capacity 3 with K / 128 = 4 nk: the INT4 decode GEMM whose loads run across
-    # tiles (gate/up nk = 4 and 6, down nk = 3; the second case's down pass,
-    # K = 768, takes the per-tile kernel)
+    # capacity 3 with K / 128 = 4 nk: the INT4 / fp8 decode GEMM whose loads run
+    # across tiles (gate/up nk = 4 and 6, down nk = 3; the second case's down
+    # pass, K = 768, takes the per-tile kernel)
     "int4_pipe": WK["skewed_int4_decode"].replace(name="i4p", T=50, d=2048, E=32, F=1536),
     "int4_pipe6": WK["skewed_int4_decode"].replace(name="i4p6", T=40, d=3072, E=32, F=768),
+    "fp8_pipe": WK["skewed_fp8_decode"].replace(name="f8p", T=50, d=2048, E=32, F=1536),
+    "fp8_pipe6": WK["skewed_fp8_decode"].replace(name="f8p6", T=40, d=3072, E=32, F=768),
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
