@@ -476,6 +476,20 @@ __global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __
   // 16-byte chunk c = (k % 32) / 8 at slot c ^ ((row >> 1) & 3)
   // (the LDS bound caps kslice * EP at 16384: at most four 8-k chunks per thread,
   // whose 32 loads all go out before any is used)
+  // x fragments: rows wv * 32 + lane % 16 (+ 16), k group lane / 16 of each step
+  const int kg = lane >> 4;
+  const uint16_t* xa0 = x + (size_t)min(wv * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const uint16_t* xa1 = x + (size_t)min(wv * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
+  constexpr int kPreSteps = 8;
+  bf16x8_t xp0[kPreSteps], xp1[kPreSteps];
+  if (ksteps <= kPreSteps) {
+#pragma unroll
+    for (int ks = 0; ks < kPreSteps; ++ks)
+      if (ks < ksteps) {
+        xp0[ks] = *(const bf16x8_t*)(xa0 + ks * 32);
+        xp1[ks] = *(const bf16x8_t*)(xa1 + ks * 32);
+      }
+  }
   const int nchunks = kslice / 8;
   float wv8[4][8];
 #pragma unroll
@@ -521,23 +535,13 @@ __global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __
     }
   }
   // ---- the MFMA loop of router_mfma_kernel over the resident stages
-  const int kg = lane >> 4;
-  const uint16_t* xa0 = x + (size_t)min(wv * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
-  const uint16_t* xa1 = x + (size_t)min(wv * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
   const uint32_t bfrag = (uint32_t)((lane & 15) * 64 + ((kg ^ (((lane & 15) >> 1) & 3)) * 16));
   f32x4_t acc[2][NF];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int n = 0; n < NF; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  bf16x8_t a0 = *(const bf16x8_t*)xa0, a1 = *(const bf16x8_t*)xa1;
-  __syncthreads();  // the split slice is in LDS
-  for (int ks = 0; ks < ksteps; ++ks) {
-    bf16x8_t n0 = a0, n1 = a1;
-    if (ks + 1 < ksteps) {
-      n0 = *(const bf16x8_t*)(xa0 + (ks + 1) * 32);
-      n1 = *(const bf16x8_t*)(xa1 + (ks + 1) * 32);
-    }
+  auto step = [&](int ks, const bf16x8_t& a0, const bf16x8_t& a1) {
     const uint8_t* st = smem + (size_t)ks * STAGE;
 #pragma unroll
     for (int n = 0; n < NF; ++n) {
@@ -551,8 +555,27 @@ __global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __
       acc[0][n] = mfma16x16x32(a0, bl, acc[0][n]);
       acc[1][n] = mfma16x16x32(a1, bl, acc[1][n]);
     }
-    a0 = n0;
-    a1 = n1;
+  };
+  if (ksteps <= kPreSteps) {
+    // the slice's x fragments were all requested before the split (above): the
+    // loop waits for memory once, not once per step
+    __syncthreads();  // the split slice is in LDS
+#pragma unroll
+    for (int ks = 0; ks < kPreSteps; ++ks)
+      if (ks < ksteps) step(ks, xp0[ks], xp1[ks]);
+  } else {
+    bf16x8_t a0 = *(const bf16x8_t*)xa0, a1 = *(const bf16x8_t*)xa1;
+    __syncthreads();  // the split slice is in LDS
+    for (int ks = 0; ks < ksteps; ++ks) {
+      bf16x8_t n0 = a0, n1 = a1;
+      if (ks + 1 < ksteps) {
+        n0 = *(const bf16x8_t*)(xa0 + (ks + 1) * 32);
+        n1 = *(const bf16x8_t*)(xa1 + (ks + 1) * 32);
+      }
+      step(ks, a0, a1);
+      a0 = n0;
+      a1 = n1;
+    }
   }
   float* out = part + (size_t)blockIdx.y * T * EP;
 #pragma unroll
