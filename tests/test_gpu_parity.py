@@ -264,11 +264,12 @@ def _check_reroute(sh, idx, dev):
 @pytest.mark.parametrize("T,E,k,D,cf,dup", [(5000, 64, 2, 4, 1.0, False), (3001, 128, 2, 4, 1.25, False),
                                             (2500, 32, 4, 8, 0.8, False), (1800, 64, 8, 3, 1.0, False),
                                             (4000, 64, 2, 6, 1.0, True), (257, 16, 3, 2, 0.5, True),
-                                            (2000, 256, 8, 4, 1.0, False)])
+                                            (2000, 256, 8, 4, 1.0, False), (20000, 128, 2, 4, 1.25, False)])
 def test_reroute_many_blocks_matches_oracle(T, E, k, D, cf, dup, dev):
-    """Re-routing over several 256-token blocks: skewed expert picks (each
-    token's top-k and fallbacks distinct, drawn with weights ~ u^3), or lists
-    with repeated fallback entries, bit-exact against the oracle's serial rule."""
+    """Re-routing over several 256-token blocks (up to 79: more than the 64 whose
+    counts one pass of the prefix sum reads): skewed expert picks (each token's
+    top-k and fallbacks distinct, drawn with weights ~ u^3), or lists with
+    repeated fallback entries, bit-exact against the oracle's serial rule."""
     rng = np.random.default_rng(T * 7 + E + k + D)
     p = rng.random(E) ** 3
     p /= p.sum()
