@@ -104,6 +104,19 @@ struct WSet {
   uint32_t q[kNF][Codec<WT, 16>::NQ > 0 ? Codec<WT, 16>::NQ : 1];
 };
 
+// The k chunk (8 values: 16 bytes of a bf16 activation row) that lane group
+// g4 holds in sub-step s.  A lane's weight bytes of a step are its 16-byte
+// loads u at byte 64 u + 16 g4 of the row's step, so each load instruction
+// covers 64 contiguous bytes of its 16 rows; sub-step s takes bf16: load s;
+// fp8: half s & 1 of load s >> 1; INT4: word s of the one load.  The
+// activation fragments are read at the same k, so each MFMA pairs equal k.
+template <int WT>
+__device__ __forceinline__ int kchunk(int g4, int s) {
+  if constexpr (WT == WT_BF16) return 4 * s + g4;
+  else if constexpr (WT == WT_FP8) return 8 * (s >> 1) + 2 * g4 + (s & 1);
+  else return 4 * g4 + s;
+}
+
 // 8 bf16 of sub-step s from a lane's raw weight registers of one fragment
 template <int WT>
 __device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Codec<WT, 16>::RAW], int s) {
@@ -179,7 +192,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
         const uint32_t src = p.gather ? (uint32_t)p.gather[tr.row0 + rr] : (uint32_t)rr;
         a_off[i] = src * (uint32_t)K * 2u + (uint32_t)(c * 16);
       }
-      // weights: fragment j's row for this lane; lane group g4 holds k = 32 g4 .. + 31 of a step
+      // weights: fragment j's row for this lane, at byte 16 g4 of each 64-byte part of a step
       const uint8_t* b_row[kNF];
       const uint32_t* q_row[kNF];
 #pragma unroll
@@ -197,7 +210,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
           qbase = p.S0;
         }
         const size_t row = (size_t)g * N + wrow;
-        b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * (CD::STEP_BYTES / 4);
+        b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
         q_row[j] = (const uint32_t*)qbase + row * KG;
       }
       // Steps past this wave's last (prefetches near the end) still issue their
@@ -219,7 +232,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
         for (int j = 0; j < kNF; ++j)
 #pragma unroll
           for (int u = 0; u < CD::RAW; ++u)
-            d.w[j][u] = *(const uint4*)(live ? b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 16 : (const uint8_t*)p.B0);
+            d.w[j][u] = *(const uint4*)(live ? b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 64 : (const uint8_t*)p.B0);
         if constexpr (CD::NQ > 0) {
 #pragma unroll
           for (int j = 0; j < kNF; ++j) d.q[j][0] = live ? q_row[j][kc] : *(const uint32_t*)p.S0;
@@ -246,7 +259,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
         f32x4_t t[kNF], rs = zero4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ (r16 % AR)) * 16);
+          const uint32_t slot = (uint32_t)((kchunk<WT>(g4, s) ^ (r16 % AR)) * 16);
           const bf16x8_t af = *(const bf16x8_t*)(st + afrag + slot);
           bf16x8_t bf[kNF];
 #pragma unroll
@@ -461,7 +474,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
         qbase = p.S0;
       }
       const size_t row = (size_t)tr.g * N + wrow;
-      b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * (CD::STEP_BYTES / 4);
+      b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
       q_row[j] = (const uint32_t*)qbase + row * KG;
     }
     if constexpr (WT == WT_FP8) {
@@ -489,7 +502,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
 #pragma unroll
       for (int u = 0; u < CD::RAW; ++u)
         wr[slot][j][u] =
-            *(const uint4*)(ilive ? b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 16 : (const uint8_t*)p.B0);
+            *(const uint4*)(ilive ? b_row[j] + (size_t)kc * CD::STEP_BYTES + u * 64 : (const uint8_t*)p.B0);
     if constexpr (decltype(chunk_start)::value) {
       if constexpr (WT == WT_INT4) {
 #pragma unroll
@@ -553,7 +566,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
         f32x4_t t[kNF], rs = zero4;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ (r16 & 3)) * 16);
+          const uint32_t slot = (uint32_t)((kchunk<WT>(g4, s) ^ (r16 & 3)) * 16);
           const bf16x8_t af = *(const bf16x8_t*)(st + afrag + slot);
           if constexpr (WT == WT_INT4) {
             rs = mfma16x16x32(af, ones, s == 0 ? zero4 : rs);

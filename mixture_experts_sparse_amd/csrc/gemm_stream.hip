@@ -18,8 +18,11 @@
 //    The load counter retires loads in issue order, so a step waiting for its
 //    activations also waits for every weight load issued before them: the
 //    weights are only as far ahead in flight as the activations are;
-//  * lane group g (lane / 16) holds k = 32 g + 8 s .. + 7 in sub-step s of a
-//    step, for both operands, so each lane's weight bytes are contiguous;
+//  * a weight row's bytes of a step are read in 64-byte parts, lane group g
+//    (lane / 16) taking bytes 16 g .. 16 g + 15 of each, so every load
+//    instruction covers whole half lines; the k values that gives each lane
+//    group in each sub-step (kchunk) are read from the activations too, so
+//    every MFMA pairs equal k;
 //  * fp8 (OCP e4m3fn) codes become bf16 in registers
 //    (v_cvt_scalef32_pk_bf16_fp8, exact) and row scales multiply the f32
 //    accumulators in the epilogue;
@@ -95,9 +98,9 @@ struct WSet {
 template <int WT>
 __device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Plan<WT, 2>::RAW], int s) {
   if constexpr (WT == WT_BF16) {
-    return __builtin_bit_cast(bf16x8_t, raw[s]);  // k = 32 g + 8 s .. + 7
+    return __builtin_bit_cast(bf16x8_t, raw[s]);  // load s: 8 bf16
   } else if constexpr (WT == WT_FP8) {
-    const uint4 q = raw[s >> 1];  // 32 codes; sub-step s uses bytes 8 s .. 8 s + 7
+    const uint4 q = raw[s >> 1];  // 16 codes; sub-step s uses half s & 1
     const uint32_t lo = (s & 1) ? q.z : q.x, hi = (s & 1) ? q.w : q.y;
     uint4 o;
     o.x = fp8x2_to_bf16x2<false>(lo);
@@ -109,6 +112,20 @@ __device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Plan<WT, 2>::RAW],
     const uint4 c = raw[0];  // 32 codes; sub-step s uses word s
     return int4_frag(s == 0 ? c.x : s == 1 ? c.y : s == 2 ? c.z : c.w);
   }
+}
+
+// The k chunk (8 values: 16 bytes of a bf16 activation row) that lane group
+// g4 holds in sub-step s.  A lane's weight bytes of a step are its 16-byte
+// loads u at byte 64 u + 16 g4 of the row's step, so each load instruction
+// covers 64 contiguous bytes of its 16 rows (one half line each, every byte
+// used by that one instruction); sub-step s takes bf16: load s; fp8: half
+// s & 1 of load s >> 1; INT4: word s of the one load.  The activation
+// fragments are read at the same k, so each MFMA still pairs equal k.
+template <int WT>
+__device__ __forceinline__ int kchunk(int g4, int s) {
+  if constexpr (WT == WT_BF16) return 4 * s + g4;
+  else if constexpr (WT == WT_FP8) return 8 * (s >> 1) + 2 * g4 + (s & 1);
+  else return 4 * g4 + s;
 }
 
 template <bool GATED, int WT, int MF>
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
   // activation DMA: instruction i of wave w covers rows 4 (w A_INS + i) .. + 3;
   // lane: row (lane >> 4), slot (lane & 15) <- chunk slot ^ (row & 15)
   const int dma_r = lane >> 4;
-  // fragment read for sub-step s, m-fragment i: row 16 i + r16, chunk 4 g4 + s
+  // fragment read for sub-step s, m-fragment i: row 16 i + r16, chunk kchunk(g4, s)
   const uint32_t afrag = (uint32_t)(r16 * AROW);
 
   for (int L = xcd * chunk + jb; L < lend; L += G8) {
@@ -164,7 +181,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       const uint32_t src = p.gather ? (uint32_t)p.gather[tr.row0 + rr] : (uint32_t)rr;
       a_off[i] = src * (uint32_t)K * 2u + (uint32_t)(c * 16);
     }
-    // this lane's weight rows (one per n-fragment), k offset 32 g4
+    // this lane's weight rows (one per n-fragment), at byte 16 g4 of each 64-byte part
     const uint8_t* b_row[NF];
     const uint32_t* q_row[NF];
 #pragma unroll
@@ -182,7 +199,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
         qbase = p.S0;
       }
       const size_t row = (size_t)g * N + wrow;
-      b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * (PL::STEP_BYTES / 4);
+      b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
       q_row[j] = (const uint32_t*)qbase + row * KG;
     }
     auto issue_a = [&](int ks) {
@@ -199,7 +216,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       for (int j = 0; j < NF; ++j)
 #pragma unroll
         for (int u = 0; u < PL::RAW; ++u)
-          d.w[j][u] = *(const uint4*)(b_row[j] + (size_t)kc * PL::STEP_BYTES + u * 16);
+          d.w[j][u] = *(const uint4*)(b_row[j] + (size_t)kc * PL::STEP_BYTES + u * 64);
       if constexpr (PL::NQ > 0) {
 #pragma unroll
         for (int j = 0; j < NF; ++j) d.q[j][0] = q_row[j][kc];
@@ -229,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       f32x4_t t[MF][NF], rs[MF];
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const uint32_t slot = (uint32_t)(((4 * g4 + s) ^ r16) * 16);
+        const uint32_t slot = (uint32_t)((kchunk<WT>(g4, s) ^ r16) * 16);
         bf16x8_t af[MF], bf[NF];
 #pragma unroll
         for (int i = 0; i < MF; ++i) af[i] = *(const bf16x8_t*)(st + afrag + i * 16 * AROW + slot);
