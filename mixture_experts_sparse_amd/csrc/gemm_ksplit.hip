@@ -137,6 +137,83 @@ __device__ __forceinline__ bf16x8_t b_frag(const uint4 (&raw)[Codec<WT, 16>::RAW
   }
 }
 
+// Fragment j's weight row for this lane -- gate/up: fragments 0,1 gate rows,
+// 2,3 the matching up rows; down: four consecutive 16-row fragments -- at byte
+// 16 g4 of each 64-byte part of a step, and that row's INT4 group words.
+template <bool GATED>
+__device__ __forceinline__ void tile_weight_rows(const KsplitParams& p, const TileRef& tr, int r16, int g4,
+                                                 size_t RB, size_t KG, const uint8_t* (&b_row)[kNF],
+                                                 const uint32_t* (&q_row)[kNF]) {
+#pragma unroll
+  for (int j = 0; j < kNF; ++j) {
+    int wrow;
+    const void* base;
+    const void* qbase;
+    if (GATED) {
+      wrow = tr.nt * 32 + (j & 1) * 16 + r16;
+      base = (j < 2) ? p.B0 : p.B1;
+      qbase = (j < 2) ? p.S0 : p.S1;
+    } else {
+      wrow = tr.nt * 64 + j * 16 + r16;
+      base = p.B0;
+      qbase = p.S0;
+    }
+    const size_t row = (size_t)tr.g * p.N + wrow;
+    b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
+    q_row[j] = (const uint32_t*)qbase + row * KG;
+  }
+}
+
+// The output column of this lane's epilogue rows (gate/up: h column, written by
+// waves 0 and 1; down: y column of fragment w), whose fp8 row scales apply.
+template <bool GATED>
+__device__ __forceinline__ int tile_out_col(const TileRef& tr, int w, int r16) {
+  return GATED ? tr.nt * 32 + (w & 1) * 16 + r16 : tr.nt * 64 + w * 16 + r16;
+}
+
+// A tile's four partial sums meet in `red` ([wave][fragment][r][lane]; fixed
+// order wave 0 + 1 + 2 + 3) and the tile's outputs are written: gate/up, waves
+// 0 and 1 write h = silu(gate sc0) * (up sc1) for fragment pair (w, w + 2);
+// down, wave w writes y = fragment w times sc0.  sync(): a block barrier after
+// this wave's LDS operations, taken after the sums are written and after they
+// are read.
+template <bool GATED, typename Sync>
+__device__ __forceinline__ void tile_epilogue(const KsplitParams& p, const TileRef& tr, const f32x4_t (&acc)[kNF],
+                                              float* red, int w, int lane, float sc0, float sc1, Sync sync) {
+#pragma unroll
+  for (int j = 0; j < kNF; ++j)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red[((w * kNF + j) * 4 + r) * 64 + lane] = acc[j][r];
+  sync();
+  auto total_of = [&](int j, int r) {
+    float v = red[((0 * kNF + j) * 4 + r) * 64 + lane];
+#pragma unroll
+    for (int ww = 1; ww < 4; ++ww) v += red[((ww * kNF + j) * 4 + r) * 64 + lane];
+    return v;
+  };
+  const int rq = (lane >> 4) * 4;  // lane holds rows rq .. rq + 3 of the tile
+  const int col = tile_out_col<GATED>(tr, w, lane & 15);
+  if (GATED) {
+    if (w < 2) {
+      uint16_t* h = (uint16_t*)p.out;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = rq + r;
+        if (m < tr.rows)
+          h[(size_t)(tr.row0 + m) * p.N + col] = f32_to_bf16_rne(silu_f32(total_of(w, r) * sc0) * (total_of(w + 2, r) * sc1));
+      }
+    }
+  } else {
+    float* y = (float*)p.out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = rq + r;
+      if (m < tr.rows) y[(size_t)(tr.row0 + m) * p.N + col] = total_of(w, r) * sc0;
+    }
+  }
+  sync();
+}
+
 // AR: activation rows staged per tile, 16 (every tile) or 4 (tiles of at most 4
 // rows: fragment row r reads staged row r & 3, so rows 4-15 of the MFMA repeat
 // rows 0-3 and are never stored)
@@ -192,27 +269,9 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
         const uint32_t src = p.gather ? (uint32_t)p.gather[tr.row0 + rr] : (uint32_t)rr;
         a_off[i] = src * (uint32_t)K * 2u + (uint32_t)(c * 16);
       }
-      // weights: fragment j's row for this lane, at byte 16 g4 of each 64-byte part of a step
       const uint8_t* b_row[kNF];
       const uint32_t* q_row[kNF];
-#pragma unroll
-      for (int j = 0; j < kNF; ++j) {
-        int wrow;
-        const void* base;
-        const void* qbase;
-        if (GATED) {  // fragments 0,1: gate rows; 2,3: the matching up rows
-          wrow = tr.nt * 32 + (j & 1) * 16 + r16;
-          base = (j < 2) ? p.B0 : p.B1;
-          qbase = (j < 2) ? p.S0 : p.S1;
-        } else {
-          wrow = tr.nt * 64 + j * 16 + r16;
-          base = p.B0;
-          qbase = p.S0;
-        }
-        const size_t row = (size_t)g * N + wrow;
-        b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
-        q_row[j] = (const uint32_t*)qbase + row * KG;
-      }
+      tile_weight_rows<GATED>(p, tr, r16, g4, RB, KG, b_row, q_row);
       // Steps past this wave's last (prefetches near the end) still issue their
       // loads -- the waits count them -- but every lane reads one common address,
       // so each such instruction costs one request and no bandwidth.
@@ -306,52 +365,18 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p
       __builtin_amdgcn_s_waitcnt(kLgkm0);
     }
 
-    // ---- the four partial sums meet in LDS (the stages are free once every wave is
-    // here).  __syncthreads: LDS writes complete before the barrier, unlike a bare s_barrier
+    // ---- the four partial sums meet in LDS, in the stage memory: free once every
+    // wave is here.  __syncthreads: LDS writes complete before the barrier,
+    // unlike a bare s_barrier
     __syncthreads();
-    float* red = (float*)smem;  // [wave][fragment][r][lane]
-#pragma unroll
-    for (int j = 0; j < kNF; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[((w * kNF + j) * 4 + r) * 64 + lane] = acc[j][r];
-    __syncthreads();
-    auto total_of = [&](int j, int r) {
-      float v = red[((0 * kNF + j) * 4 + r) * 64 + lane];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) v += red[((ww * kNF + j) * 4 + r) * 64 + lane];
-      return v;
-    };
-    const int rq = g4 * 4;  // lane holds rows rq .. rq + 3 of the tile, column r16 of each fragment
-    if (GATED) {
-      if (w < 2) {  // wave j: gate fragment j and up fragment j + 2
-        const int j = w;
-        const int f = tr.nt * 32 + j * 16 + r16;
-        float sg = 1.f, su = 1.f;
-        if constexpr (WT == WT_FP8) {
-          sg = ((const float*)p.S0)[(size_t)g * N + f];
-          su = ((const float*)p.S1)[(size_t)g * N + f];
-        }
-        uint16_t* h = (uint16_t*)p.out;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = rq + r;
-          if (m < tr.rows)
-            h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(total_of(j, r) * sg) * (total_of(j + 2, r) * su));
-        }
-      }
-    } else {  // wave j: fragment j
-      const int j = w;
-      const int n = tr.nt * 64 + j * 16 + r16;
-      float sd = 1.f;
-      if constexpr (WT == WT_FP8) sd = ((const float*)p.S0)[(size_t)g * N + n];
-      float* y = (float*)p.out;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = rq + r;
-        if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = total_of(j, r) * sd;
-      }
+    float sc0 = 1.f, sc1 = 1.f;
+    if constexpr (WT == WT_FP8) {
+      const size_t at = (size_t)g * N + tile_out_col<GATED>(tr, w, r16);
+      sc0 = ((const float*)p.S0)[at];
+      sc1 = GATED ? ((const float*)p.S1)[at] : sc0;
     }
-    __syncthreads();  // the reduction area is read before the next tile's loads refill it
+    // the second barrier: the reduction area is read before the next tile's loads refill it
+    tile_epilogue<GATED>(p, tr, acc, (float*)smem, w, lane, sc0, sc1, [] { __syncthreads(); });
   }
 }
 
@@ -459,30 +484,11 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
       src = (uint32_t)(tr.row0 + min(r, tr.rows - 1));
     }
     a_src = (const uint8_t*)p.A + (size_t)src * K * 2 + c * 16;
-#pragma unroll
-    for (int j = 0; j < kNF; ++j) {
-      int wrow;
-      const void* base;
-      const void* qbase;
-      if (GATED) {  // fragments 0,1: gate rows; 2,3: the matching up rows
-        wrow = tr.nt * 32 + (j & 1) * 16 + r16;
-        base = (j < 2) ? p.B0 : p.B1;
-        qbase = (j < 2) ? p.S0 : p.S1;
-      } else {
-        wrow = tr.nt * 64 + j * 16 + r16;
-        base = p.B0;
-        qbase = p.S0;
-      }
-      const size_t row = (size_t)tr.g * N + wrow;
-      b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
-      q_row[j] = (const uint32_t*)qbase + row * KG;
-    }
-    if constexpr (WT == WT_FP8) {
-      // the epilogue's rows: gated, wave w < 2 writes h column nt 32 + 16 w + r16
-      // (gate and up scale); otherwise wave w writes y column nt 64 + 16 w + r16
-      const int col = GATED ? tr.nt * 32 + (w & 1) * 16 + r16 : tr.nt * 64 + w * 16 + r16;
-      sc_at[0] = (const float*)p.S0 + (size_t)tr.g * N + col;
-      sc_at[1] = GATED ? (const float*)p.S1 + (size_t)tr.g * N + col : sc_at[0];
+    tile_weight_rows<GATED>(p, tr, r16, g4, RB, KG, b_row, q_row);
+    if constexpr (WT == WT_FP8) {  // the row scales of this lane's epilogue column
+      const size_t at = (size_t)tr.g * N + tile_out_col<GATED>(tr, w, r16);
+      sc_at[0] = (const float*)p.S0 + at;
+      sc_at[1] = GATED ? (const float*)p.S1 + at : sc_at[0];
     }
   };
   // one step's loads, into ring slot / LDS stage `slot`: the weights of local
@@ -591,43 +597,8 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
     }
 
     // ---- the four partial sums meet in their own LDS area (the stages hold the
-    // next tile's loads in flight); fixed order wave 0 + 1 + 2 + 3
-#pragma unroll
-    for (int j = 0; j < kNF; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) red[((w * kNF + j) * 4 + r) * 64 + lane] = acc[j][r];
-    lds_barrier();
-    auto total_of = [&](int j, int r) {
-      float v = red[((0 * kNF + j) * 4 + r) * 64 + lane];
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) v += red[((ww * kNF + j) * 4 + r) * 64 + lane];
-      return v;
-    };
-    const int rq = g4 * 4;
-    if (GATED) {
-      if (w < 2) {
-        const int j = w;
-        const int f = tr.nt * 32 + j * 16 + r16;
-        uint16_t* h = (uint16_t*)p.out;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = rq + r;
-          if (m < tr.rows)
-            h[(size_t)(tr.row0 + m) * N + f] =
-                f32_to_bf16_rne(silu_f32(total_of(j, r) * st_sc[0]) * (total_of(j + 2, r) * st_sc[1]));
-        }
-      }
-    } else {
-      const int j = w;
-      const int n = tr.nt * 64 + j * 16 + r16;
-      float* y = (float*)p.out;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = rq + r;
-        if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = total_of(j, r) * st_sc[0];
-      }
-    }
-    lds_barrier();  // the partial sums are read before the next tile writes them
+    // next tile's loads in flight)
+    tile_epilogue<GATED>(p, tr, acc, red, w, lane, st_sc[0], st_sc[1], [] { lds_barrier(); });
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in LDS after the block ends
 }
