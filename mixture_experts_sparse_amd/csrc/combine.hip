@@ -9,9 +9,11 @@
 //
 //   out[t] = sum_{j: dest_row[t,j] >= 0} w[t,j] * y_perm[dest_row[t,j]]  (+ y_shared[t])
 //
-// Bandwidth-bound: one wave per token, 16-byte vector loads of the k source
-// rows (gathered by dest_row), four slots' rows in flight at once, f32 FMAs in
-// j order, one store of the row.
+// Bandwidth-bound: one wave per token (or, for few tokens, wpt waves per
+// token, each taking every wpt-th stretch of the row, so a decode batch still
+// has hundreds of waves and each makes one or two round trips), 16-byte vector
+// loads of the k source rows (gathered by dest_row), up to four slots' rows in
+// flight at once, f32 FMAs in j order, one store of the row.
 // When the down projection split its reduction, the partial sums of a row are
 // added in part order first, so the result does not depend on scheduling.
 #include <type_traits>
@@ -49,22 +51,24 @@ __device__ __forceinline__ void store_out(void* out, size_t off, const float4& a
   }
 }
 
-// One wave per token; each lane handles U 16-byte vectors of the row per trip.
-// The rows of JB slots are requested together (JB x U loads in flight per lane)
-// and then added in slot order, so the sum is the same as one slot at a time.
+// wpt waves per token; wave part of a token handles the trips part, part +
+// wpt, ... of its row, each lane U 16-byte vectors per trip.  The rows of JB
+// slots are requested together (JB x U loads in flight per lane) and then
+// added in slot order, so the sum is the same as one slot at a time.
 template <bool BF16OUT, int U, int JB>
 __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__ y_perm,
                                                       const float4* __restrict__ y_shared,
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ topk_w,
                                                       void* __restrict__ out, int T, int vec_per_row,
-                                                      int k, int64_t rows, Parts yp, Parts sp) {
+                                                      int k, int64_t rows, Parts yp, Parts sp, int wpt) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave
+  const int t = gw / wpt, part = gw - t * wpt;
   if (t >= T) return;
   const int32_t* dr = dest_row + (size_t)t * k;
   const float* wt = topk_w + (size_t)t * k;
-  for (int v0 = lane; v0 < vec_per_row; v0 += 64 * U) {
+  for (int v0 = part * 64 * U + lane; v0 < vec_per_row; v0 += 64 * U * wpt) {
     float4 acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -120,24 +124,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
 moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows) {
   if (a.T == 0) return MOE_OK;
   const int vec = a.d / 4;
-  const dim3 grid((unsigned)ceil_div(a.T, 4));
+  // waves per token: enough that a small batch fills the chip (about 512 waves),
+  // never more than the row's trips
+  const int trips = (int)ceil_div(vec, 64 * 4);
+  int wpt = 1;
+  while (wpt * 2 <= trips && (int64_t)a.T * wpt * 2 <= 512) wpt *= 2;
+  const dim3 grid((unsigned)ceil_div((int64_t)a.T * wpt, 4));
   const Parts yp{(const float4*)a.y_rest, a.y_stride / 4, a.y_split};
   const Parts sp{(const float4*)a.sh_rest, a.sh_stride / 4, a.sh_split};
   int tok = begin_launch("combine", s);
-  // slots requested together: four at a time when a token has many (measured:
-  // one at a time is faster for k <= 2, where the extra registers cost occupancy)
+  // slots requested together: four at a time when a token has many, or when a
+  // small batch leaves registers to spare (measured: one at a time is faster for
+  // k <= 2 at full occupancy, where the extra registers cost waves)
   auto go = [&](auto bf16_tag, auto jb_tag) {
     constexpr bool B = decltype(bf16_tag)::value;
     constexpr int JB = decltype(jb_tag)::value;
     hipLaunchKernelGGL((combine_kernel<B, 4, JB>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
-                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp);
+                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp, wpt);
   };
   using I1 = std::integral_constant<int, 1>;
   using I4 = std::integral_constant<int, 4>;
+  const bool one = a.k <= 2 && wpt == 1;
   if (a.out_dtype == MOE_BF16) {
-    if (a.k <= 2) go(std::true_type{}, I1{}); else go(std::true_type{}, I4{});
+    if (one) go(std::true_type{}, I1{}); else go(std::true_type{}, I4{});
   } else {
-    if (a.k <= 2) go(std::false_type{}, I1{}); else go(std::false_type{}, I4{});
+    if (one) go(std::false_type{}, I1{}); else go(std::false_type{}, I4{});
   }
   return end_launch(tok, s);
 }

@@ -590,30 +590,36 @@ __global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __
     }
 }
 
-// one wave per token: z = sum of the d-slice partials in order, then route_token
-template <int EPL>
+// one wave per token: z = sum of the d-slice partials in order, then route_token.
+// The partials of the lane's experts are requested PB slices at a time and
+// then added in slice order: PB = 32 for small batches (one memory round trip
+// for a decode batch), 8 otherwise (fewer registers, more waves per SIMD).
+template <int EPL, int PB>
 __global__ __launch_bounds__(256) void topk_kernel(RouteLaunch a) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= a.T) return;
-  const float* part = a.part;
-  const int S = a.split, EP = a.ep, T = a.T;
-  route_token<EPL>(a, t, lane, [&](int e) {
-    // partials added in split order; loads issued eight at a time
-    const float* pe = part + (size_t)t * EP + e;
-    const size_t st = (size_t)T * EP;
-    float z = 0.f;
-    int sp = 0;
-    for (; sp + 8 <= S; sp += 8) {
-      float v[8];
+  const int S = a.split, EP = a.ep, T = a.T, E = a.E;
+  const size_t st = (size_t)T * EP;
+  float zv[EPL];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) v[q] = pe[(size_t)(sp + q) * st];
+  for (int i = 0; i < EPL; ++i) zv[i] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += PB) {
+    float v[EPL][PB];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) z += v[q];
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      const float* pe = a.part + (size_t)t * EP + e;
+#pragma unroll
+      for (int q = 0; q < PB; ++q) v[i][q] = (s0 + q < S && e < E) ? pe[(size_t)(s0 + q) * st] : 0.f;
     }
-    for (; sp < S; ++sp) z += pe[(size_t)sp * st];
-    return z;
-  });
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+#pragma unroll
+      for (int q = 0; q < PB; ++q)
+        if (s0 + q < S) zv[i] += v[i][q];
+  }
+  route_token<EPL>(a, t, lane, [&](int e) { return zv[(e - lane) >> 6]; });
 }
 
 template <int EP>
@@ -631,7 +637,7 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
     moe_status st = end_launch(tok, s);
     if (st != MOE_OK) return st;
     tok = begin_launch("route_topk", s);
-    hipLaunchKernelGGL(topk_kernel<(EP + 63) / 64>, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 32>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
     return end_launch(tok, s);
   }
   int tok = begin_launch("router_prep", s);
@@ -645,7 +651,10 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   st = end_launch(tok, s);
   if (st != MOE_OK) return st;
   tok = begin_launch("route_topk", s);
-  hipLaunchKernelGGL(topk_kernel<(EP + 63) / 64>, dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+  if (a.T <= 256)
+    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 32>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 8>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
   return end_launch(tok, s);
 }
 
