@@ -33,6 +33,7 @@
 #include <float.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "route_keys.h"
@@ -627,10 +628,18 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   const int kslice = a.d / a.split;
   const size_t fused_lds = (size_t)(kslice / 32) * 3 * EP * 64;
   if (a.T <= 256 && fused_lds <= kFusedRouterLds && (size_t)kslice * EP <= 16384) {
-    // more than 64 KB of dynamic LDS needs the attribute (set on the current device)
-    if (hipFuncSetAttribute((const void*)router_fused_kernel<EP>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)kFusedRouterLds) != hipSuccess)
-      return fail(MOE_ERR_HIP, "hipFuncSetAttribute(router_fused_kernel) failed");
+    // more than 64 KB of dynamic LDS needs the attribute, set once per device
+    // (a repeat after a race between threads is harmless)
+    static std::atomic<bool> lds_set[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+      return fail(MOE_ERR_HIP, "hipGetDevice failed or device id out of range");
+    if (!lds_set[dev].load(std::memory_order_acquire)) {
+      if (hipFuncSetAttribute((const void*)router_fused_kernel<EP>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              (int)kFusedRouterLds) != hipSuccess)
+        return fail(MOE_ERR_HIP, "hipFuncSetAttribute(router_fused_kernel) failed");
+      lds_set[dev].store(true, std::memory_order_release);
+    }
     int tok = begin_launch("router_mfma", s);
     hipLaunchKernelGGL(router_fused_kernel<EP>, dim3(1, a.split), dim3(512), fused_lds, s, (const uint16_t*)a.x,
                        a.w_router, a.part, a.T, a.d, a.E, kslice);
