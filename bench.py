@@ -34,6 +34,9 @@ PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0, "f32": 157.3}
 DEFAULT_WORKLOAD = "mixtral_bf16"
 
 
+SETTLE_MS = 100.0  # untimed load before the timed steps, at least (warm-up + settle steps)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -48,6 +51,9 @@ def parse():
     ap.add_argument("--balance", action="store_true",
                     help="each step also runs the load-balancing statistics and the bias step "
                          "(moe_router_stats, moe_bias_update on a scratch bias)")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of a HIP graph holding one step per weight copy "
+                         "(the serving mode for decode) instead of stream launches")
     ap.add_argument("--weight-copies", type=int, default=0,
                     help="expert-weight copies the steps rotate through (0: 3 when T <= 1024, else 1), "
                          "so a small step's weights are not served from the 256 MB MALL")
@@ -232,15 +238,67 @@ def main():
             L.moe_router_stats(cfg, routing["logits"], inp.bias, inp.gumbel_u, counts, prob_mean, aux, ws)
             L.moe_bias_update(cfg, counts, scratch_bias)
 
+    w0 = torch.cuda.Event(enable_timing=True)
+    w1 = torch.cuda.Event(enable_timing=True)
+    w0.record()
     for i in range(args.warmup):
         step(i)
+    w1.record()
     torch.cuda.synchronize()
-    # timed region: K steps, one event between steps and none inside them
-    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    # the clocks need about 100 ms of load to settle: when the W warm-up steps
+    # are shorter than that (decode-sized steps), more untimed steps follow
+    warm_ms = w0.elapsed_time(w1) if args.warmup else 0.0
+    per_ms = warm_ms / args.warmup if args.warmup else 0.0
+    settle = 0
+    if warm_ms < SETTLE_MS:
+        if per_ms <= 0.0:  # no warm-up steps: time one
+            w0.record()
+            step(0)
+            w1.record()
+            torch.cuda.synchronize()
+            per_ms = max(w0.elapsed_time(w1), 1e-3)
+            warm_ms, settle = per_ms, 1
+        n = min(20000, int((SETTLE_MS - warm_ms) / per_ms) + 1)
+        for i in range(n):
+            step(i)
+        torch.cuda.synchronize()
+        settle += n
+    if args.graph:
+        # one graph holds one step per weight copy (the library makes no
+        # allocation, copy, fill or synchronisation, so a step captures as is)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                step(i)
+        for _ in range(max(1, args.warmup // copies)):
+            graph.replay()
+        torch.cuda.synchronize()
+        n_calls, per_call = max(1, args.steps // copies), copies
+
+        def run_one(i):
+            graph.replay()
+    else:
+        n_calls, per_call = args.steps, 1
+
+        def run_one(i):
+            step(args.warmup + i)
+    timed_steps = n_calls * per_call
+    # timed region: K steps with an event only at each end (an event between
+    # steps lengthens a decode-sized step by a few microseconds)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    t_start.record()
+    for i in range(n_calls):
+        run_one(i)
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    # step-time spread: the same steps again, one event after each
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)]
     marks[0].record()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    for i in range(n_calls):
+        run_one(i)
         marks[i + 1].record()
     torch.cuda.synchronize()
     # per-kernel durations: the same K steps again, with the library's event pair
@@ -253,9 +311,8 @@ def main():
     torch.cuda.synchronize()
     L.moe_profile_enable(False)
     prof = L.moe_profile_read()
-    ms_total = marks[0].elapsed_time(marks[-1])
-    ms_step = ms_total / args.steps
-    step_times = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    ms_step = ms_total / timed_steps
+    step_times = np.array([marks[i].elapsed_time(marks[i + 1]) / per_call for i in range(n_calls)])
     st = stats.cpu().numpy()
     kept = int(st[sh.E:2 * sh.E].sum())
     touched = int((st[sh.E:2 * sh.E] > 0).sum())
@@ -306,8 +363,9 @@ def main():
         "value": round(sh.T / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": timed_steps,
         "warmup": args.warmup,
+        "settle_steps": settle,
         "ms_per_step": round(ms_step, 4),
         "step_ms": {"p10": round(float(np.percentile(step_times, 10)), 4),
                     "median": round(float(np.median(step_times)), 4),
@@ -321,7 +379,8 @@ def main():
                    "n_shared": sh.n_shared, "weights": dt_name, "router": "f32",
                    "capacity_factor": sh.capacity_factor or None, "kept_rows": kept,
                    "touched_experts": touched, "dropped": int(st[2 * sh.E]),
-                   "weight_copies": copies, "balance": bool(args.balance)},
+                   "weight_copies": copies, "balance": bool(args.balance),
+                   "launch": "hip_graph" if args.graph else "stream"},
         "roofline": roof,
         "kernels": kernels,
     }
