@@ -46,6 +46,10 @@
  *    exception crosses this interface.
  *  - Results are deterministic: no atomic decides any order or any sum, so two
  *    calls on the same inputs give bit-identical outputs.
+ *  - Entry points may be called from several host threads at once.  Calls
+ *    that run concurrently (on different streams) need workspaces and output
+ *    buffers of their own; calls that share a workspace must be ordered on one
+ *    stream.
  *  - Expert weights are stored [out, in] (reduction dimension contiguous):
  *    W_gate, W_up are [E, F, d], W_down is [E, d, F].  fp8 weights are OCP
  *    e4m3fn codes with one float32 scale per output row ([E,F], [E,F], [E,d]).
