@@ -138,7 +138,7 @@ def topk_by_keys(keys: np.ndarray, k: int):
     """Top-k of each row: descending key, ties to the lower expert index.
 
     [P3] s3.1 asks for the k largest, sorted; the tie rule is a reading
-    reading (torch leaves it open).  Uses a stable sort of -key as the library
+    of its own (torch leaves it open).  Uses a stable sort of -key as the library
     step.  Also returns, per token, the selection gap (k-th key minus the
     (k+1)-th) and the order gap (smallest difference between consecutive chosen
     keys), both in float64, so callers can set near-ties aside.
