@@ -77,6 +77,11 @@ SMALL = {
     "odd_experts": WK["mixtral_bf16"].replace(name="odd", T=77, d=128, E=5, k=3, F=64),
     "dense_E1": WK["mixtral_bf16"].replace(name="dense", T=130, d=256, E=1, k=1, F=128),
     "k_equals_E": WK["mixtral_bf16"].replace(name="kE", T=90, d=128, E=8, k=8, F=128),
+    # maximum sizes: every token to all 256 experts; and k = E under a capacity
+    # limit that keeps the first half of every expert's pairs
+    "k_max": WK["mixtral_bf16"].replace(name="kmax", T=20, d=128, E=256, k=256, F=64),
+    "k_equals_E_cap": WK["mixtral_bf16"].replace(name="kEc", T=50, d=128, E=64, k=64, F=64,
+                                                  capacity_factor=0.5),
     "single_token": WK["mixtral_bf16"].replace(name="one", T=1, d=256, E=8, k=2, F=128),
     "f32_ragged": WK["tiny_fp32"].replace(name="f32r", T=203, d=256, E=6, k=2, F=96),
 }
