@@ -79,6 +79,46 @@ def m_bias_in_weights(z, rc, bias=None, u=None):
     return key, basis
 
 
+def _softmax_keys_variant(z, rc, bias, u, *, noise_tempered=True, logit_bias_tempered=True,
+                          select_bias_tempered=False):
+    """selection_keys for softmax scoring with the temperature placed elsewhere."""
+    if rc.score != O.SCORE_SOFTMAX:
+        return _orig["selection_keys"](z, rc, bias, u)
+    f32 = np.float32
+    z32 = np.asarray(z, f32)
+    b32 = None if bias is None else np.asarray(bias, f32)[None, :]
+    g = None if u is None else O.gumbel_noise(u)
+    inner = z32.copy()
+    if rc.bias_mode == O.BIAS_LOGIT and logit_bias_tempered:
+        inner = (inner + b32).astype(f32)
+    if g is not None and noise_tempered:
+        inner = (inner + g).astype(f32)
+    l = (inner / f32(rc.tau)).astype(f32)
+    if rc.bias_mode == O.BIAS_LOGIT and not logit_bias_tempered:
+        l = (l + b32).astype(f32)
+    if g is not None and not noise_tempered:
+        l = (l + g).astype(f32)
+    key = l
+    if rc.bias_mode == O.BIAS_SELECT_ONLY:
+        key = (((l * f32(rc.tau)) + b32) / f32(rc.tau)).astype(f32) if select_bias_tempered else (l + b32).astype(f32)
+    return key, l
+
+
+def m_tau_divides_logit_only(z, rc, bias=None, u=None):
+    """l = z / tau + g: the noise escapes the temperature."""
+    return _softmax_keys_variant(z, rc, bias, u, noise_tempered=False)
+
+
+def m_logit_bias_untempered(z, rc, bias=None, u=None):
+    """l = (z + g) / tau + b: the logit bias escapes the temperature."""
+    return _softmax_keys_variant(z, rc, bias, u, logit_bias_tempered=False)
+
+
+def m_select_bias_tempered(z, rc, bias=None, u=None):
+    """key = (z + g + b) / tau for a selection-only bias."""
+    return _softmax_keys_variant(z, rc, bias, u, select_bias_tempered=True)
+
+
 def m_probs_with_selection_bias(z, rc, bias=None, u=None):
     key, _ = O.selection_keys(z, rc, bias, u)
     k = np.asarray(key, np.float64)
@@ -239,6 +279,11 @@ MUTATIONS = [
     ("combine", m_combine_unweighted, ["test_identity_expert_combine_inverts_permute"]),
     ("fp8_e4m3fn_decode", m_fp8_bias8, ["test_fp8_decode_all_codes"]),
     ("selection_keys", m_bias_in_weights, ["test_selection_only_bias_steers_but_does_not_weigh"]),
+    ("selection_keys", m_tau_divides_logit_only, ["test_temperature_divides_logit_plus_noise",
+                                                  "test_logit_bias_noise_and_temperature_together"]),
+    ("selection_keys", m_logit_bias_untempered, ["test_logit_bias_is_tempered_with_the_logit",
+                                                 "test_logit_bias_noise_and_temperature_together"]),
+    ("selection_keys", m_select_bias_tempered, ["test_selection_only_bias_is_added_after_the_temperature"]),
     ("router_probs", m_probs_with_selection_bias,
      ["test_router_probs_ignore_selection_only_bias_and_follow_logit_bias"]),
     ("router_probs", m_probs_no_tau, ["test_router_probs_are_the_unrenormalised_gate_weights"]),

@@ -212,6 +212,82 @@ def test_logit_bias_enters_softmax():
     np.testing.assert_allclose(route.w[0], [0.75, 0.25], rtol=1e-6)
 
 
+def _uniform_for_noise(c):
+    """u = exp(-exp(-c)) as float32, so that -log(-log u) = c up to the rounding
+    of u; returns u and a bound on |g - c| from that rounding."""
+    c = np.asarray(c, np.float64)
+    u64 = np.exp(-np.exp(-c))
+    u = u64.astype(np.float32)
+    slope = 1.0 / (u64 * np.exp(-c))          # |dg/du| at u
+    return u, float(np.max(slope * np.abs(u.astype(np.float64) - u64))) + 1e-7
+
+
+def test_temperature_divides_logit_plus_noise():
+    """Page P1 (mlqm.cn) s3.1: the perturbed logits are (z + g) / tau, then the
+    softmax.  Hand case, tau = 0.5, Gumbel noise fixed to known values:
+    z = (0, 1, 0, 0), g = (1.2, 0, 0.9, 0) -> l = (2.4, 2.0, 1.8, 0).  The top-2
+    is (0, 1) in that order, and without renormalisation (the Gumbel workload)
+    the weights are e^2.4 / S and e^2.0 / S with S = e^2.4 + e^2 + e^1.8 + 1.
+    Dividing only z by tau (z / tau + g = (1.2, 2.0, 0.9, 0)) reverses the order."""
+    z = np.array([[0.0, 1.0, 0.0, 0.0]], np.float32)
+    u, gerr = _uniform_for_noise([[1.2, 0.0, 0.9, 0.0]])
+    rc = O.RouteConfig(E=4, k=2, tau=0.5, renormalize=0)
+    route = O.route_from_logits(z, rc, u=u)
+    assert list(route.idx[0]) == [0, 1]
+    S = math.exp(2.4) + math.exp(2.0) + math.exp(1.8) + 1.0
+    # each l moves by at most 2 gerr (1/tau), so each weight by about 4 gerr relative
+    np.testing.assert_allclose(route.w[0], [math.exp(2.4) / S, math.exp(2.0) / S], rtol=8 * gerr + 1e-6)
+    np.testing.assert_allclose(route.keys[0], [2.4, 2.0, 1.8, 0.0], atol=4 * gerr + 1e-6)
+    # renormalised over the chosen two: e^0.4 / (e^0.4 + 1)
+    rc1 = O.RouteConfig(E=4, k=2, tau=0.5, renormalize=1)
+    w1 = O.route_from_logits(z, rc1, u=u).w[0]
+    p = math.exp(0.4) / (math.exp(0.4) + 1.0)
+    np.testing.assert_allclose(w1, [p, 1.0 - p], rtol=8 * gerr + 1e-6)
+
+
+def test_logit_bias_is_tempered_with_the_logit():
+    """A logit bias is part of the logit, so the temperature divides it too:
+    l = (z + b) / tau.  z = 0, b = (0, ln 3, -10), tau = 0.5 -> l = (0, 2 ln 3,
+    -20): the top-2 is (1, 0) with renormalised weights 9/10, 1/10 (a bias added
+    after the temperature would give 3/4, 1/4)."""
+    z = np.zeros((1, 3), dtype=np.float32)
+    b = np.array([0.0, math.log(3.0), -10.0], np.float32)
+    rc = O.RouteConfig(E=3, k=2, tau=0.5, bias_mode=O.BIAS_LOGIT)
+    route = O.route_from_logits(z, rc, bias=b)
+    assert list(route.idx[0]) == [1, 0]
+    np.testing.assert_allclose(route.w[0], [0.9, 0.1], rtol=1e-6)
+
+
+def test_logit_bias_noise_and_temperature_together():
+    """All three at once: l = (z + b + g) / tau.  z = (0.5, 0, 0), b = (0, 0.25,
+    0), g = (0, 0.5, -0.5), tau = 0.25 -> l = (2, 3, -2); renormalised top-2 is
+    (1, 0) with weights e / (e + 1), 1 / (e + 1)."""
+    z = np.array([[0.5, 0.0, 0.0]], np.float32)
+    b = np.array([0.0, 0.25, 0.0], np.float32)
+    u, gerr = _uniform_for_noise([[0.0, 0.5, -0.5]])
+    rc = O.RouteConfig(E=3, k=2, tau=0.25, bias_mode=O.BIAS_LOGIT)
+    route = O.route_from_logits(z, rc, bias=b, u=u)
+    assert list(route.idx[0]) == [1, 0]
+    p = math.e / (math.e + 1.0)
+    np.testing.assert_allclose(route.w[0], [p, 1.0 - p], rtol=16 * gerr + 1e-6)
+    np.testing.assert_allclose(route.keys[0], [2.0, 3.0, -2.0], atol=8 * gerr + 1e-6)
+
+
+def test_selection_only_bias_is_added_after_the_temperature():
+    """With softmax scoring, a selection-only bias steers the choice and is not
+    part of the logit: key = (z + g) / tau + b, weights from (z + g) / tau.
+    z = (0, 1, 0.5), tau = 0.5, b = (1.5, 0, 0): l = (0, 2, 1), keys = (1.5, 2, 1):
+    the top-2 is (1, 0) and the renormalised weights are e^2 / (e^2 + 1), 1 / (e^2 + 1).
+    A bias divided by tau as well (keys (3, 2, 1)) puts expert 0 first."""
+    z = np.array([[0.0, 1.0, 0.5]], np.float32)
+    b = np.array([1.5, 0.0, 0.0], np.float32)
+    rc = O.RouteConfig(E=3, k=2, tau=0.5, bias_mode=O.BIAS_SELECT_ONLY)
+    route = O.route_from_logits(z, rc, bias=b)
+    assert list(route.idx[0]) == [1, 0]
+    e2 = math.exp(2.0)
+    np.testing.assert_allclose(route.w[0], [e2 / (e2 + 1.0), 1.0 / (e2 + 1.0)], rtol=1e-6)
+
+
 # ---------------------------------------------------------------- S3 capacity
 def test_capacity_worked_examples_from_pages():
     with open(os.path.join(GOLDEN, "capacity_examples.json")) as f:
