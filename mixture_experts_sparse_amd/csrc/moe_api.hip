@@ -141,13 +141,17 @@ moe_status check_config(const moe_config* c) {
 }
 
 // C = max(1, floor(T*k/E*cf)) in double from the float32 factor; -1 = no limit.
+// No expert can receive more than T*k pairs, so any C at or above that limits
+// nothing: C is clamped there before the conversion, which keeps C and C*E in
+// range for every finite factor without changing a result.
 static_assert(sizeof(moe_config) == 17 * 4, "moe_config layout is part of the ABI");
 static_assert(sizeof(moe_expert_weights) == 12 * 8, "moe_expert_weights layout is part of the ABI");
 
 int64_t capacity_of(const moe_config* c) {
   if (!(c->capacity_factor > 0.f)) return -1;
   const double v = std::floor((double)c->T * (double)c->top_k / (double)c->E * (double)c->capacity_factor);
-  return v < 1.0 ? 1 : (int64_t)v;
+  const double most = std::max(1.0, (double)c->T * (double)c->top_k);
+  return v < 1.0 ? 1 : (int64_t)std::min(v, most);
 }
 
 int64_t perm_rows(const moe_config* c) {

@@ -163,3 +163,18 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     mod = importlib.import_module("mixture_experts_sparse_amd")
     with pytest.raises(ImportError):
         mod.load()
+
+
+@pytest.mark.parametrize("cf", [1e15, 1e30, 3.0e38])
+def test_huge_capacity_factor_limits_nothing(L, cf):
+    """A finite but enormous capacity factor makes C larger than any expert can
+    be offered (T*k pairs): it must act as no limit, with every pair kept and
+    the same row count and workspace as without a limit -- not an overflowed
+    negative C * E."""
+    s = W.WORKLOADS["fine_shared_bf16"]
+    unlimited = L.make_config(s.replace(capacity_factor=0.0))
+    huge = L.make_config(s.replace(capacity_factor=cf))
+    assert L.permuted_rows(huge) == s.T * s.k == L.permuted_rows(unlimited)
+    assert L.workspace_bytes(huge) == L.workspace_bytes(unlimited)
+    tiny = L.make_config(s.replace(T=1, capacity_factor=cf))
+    assert L.permuted_rows(tiny) == s.k
