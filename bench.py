@@ -158,9 +158,29 @@ def kernel_key(name: str) -> str:
     return name
 
 
-def cpu_baseline(inp, sample: int):
-    """Time the CPU oracle (as it stands) on the first `sample` tokens."""
-    import numpy as np
+def host_cpu():
+    """Logical CPUs this process may run on, and the CPU model name."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(inp, sample: int, one_thread_s: float = 10.0):
+    """Time the CPU oracle (as it stands) on the first `sample` tokens with every
+    BLAS thread, then on a smaller first slice with one thread (sized to take
+    about `one_thread_s` seconds)."""
+    import numpy as np  # noqa: F401
     import threadpoolctl
 
     from oracle import from_inputs as FI
@@ -168,20 +188,32 @@ def cpu_baseline(inp, sample: int):
 
     sh = inp.shape
     cpu = inp.to("cpu")
-    x = FI.to_np(cpu.x)[:sample]
-    u = FI.to_np(cpu.gumbel_u)
-    u = None if u is None else u[:sample]
     ew = FI.expert_weights(cpu)
     shw = FI.shared_weights(cpu)
     wr, b = FI.to_np(cpu.w_router), FI.to_np(cpu.bias)
-    spec = FI.layer_spec(sh.replace(T=sample))
-    t0 = time.perf_counter()
-    O.forward(spec, x, wr, ew, shw, b, u)
-    dt = time.perf_counter() - t0
+    x_all = FI.to_np(cpu.x)
+    u_all = FI.to_np(cpu.gumbel_u)
+
+    def run(n):
+        x = x_all[:n]
+        u = None if u_all is None else u_all[:n]
+        spec = FI.layer_spec(sh.replace(T=n))
+        t0 = time.perf_counter()
+        O.forward(spec, x, wr, ew, shw, b, u)
+        return time.perf_counter() - t0
+
     threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] or [1])
+    dt = run(sample)
+    n1 = int(max(16, min(sample, sample * one_thread_s / max(dt * threads, 1e-9))))
+    with threadpoolctl.threadpool_limits(1):
+        dt1 = run(n1)
+    nproc, model = host_cpu()
     return {"value": sample / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {sample} of {sh.T} tokens of {sh.name} (capacity recomputed for the "
-                      f"sample), full layer in float64 numpy; {dt:.2f} s wall"}
+                      f"sample), full layer in float64 numpy; {dt:.2f} s wall with {threads} BLAS "
+                      f"threads",
+            "nproc": nproc, "cpu_model": model, "wall_s": round(dt, 3),
+            "one_thread": {"value": n1 / dt1, "unit": "tokens/s", "tokens": n1, "wall_s": round(dt1, 3)}}
 
 
 def main():

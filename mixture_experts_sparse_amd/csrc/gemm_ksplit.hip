@@ -49,25 +49,14 @@ constexpr unsigned kLgkm0 = 0xC07Fu;  // lgkmcnt(0) alone
 __device__ __forceinline__ void issue_fence() { asm volatile("" ::: "memory"); }
 
 // blocks per CU the registers and LDS are sized for, and the prefetch distances
-#ifndef KS_OCC
-#define KS_OCC 2
-#endif
-#ifndef KS_PD_BF16
-#define KS_PD_BF16 2
-#endif
-#ifndef KS_PD_FP8
-#define KS_PD_FP8 3
-#endif
-#ifndef KS_PD_INT4
-#define KS_PD_INT4 4
-#endif
+// in K steps per weight type
+constexpr int kOcc = 2;
+constexpr int kPdBf16 = 2;
+constexpr int kPdFp8 = 3;
+constexpr int kPdInt4 = 4;
 // with at most 4 rows per expert (capacity 1-4: decode) only those rows are staged
-#ifndef KS_PD4_FP8
-#define KS_PD4_FP8 3
-#endif
-#ifndef KS_PD4_INT4
-#define KS_PD4_INT4 4
-#endif
+constexpr int kPd4Fp8 = 3;
+constexpr int kPd4Int4 = 4;
 
 enum { WT_BF16 = 0, WT_FP8 = 1, WT_INT4 = 2 };
 
@@ -79,9 +68,9 @@ struct Codec {
   // prefetch distance D in steps, for the weights (registers) and the activations
   // (D + 1 LDS stages per wave) alike: the waits count loads in issue order, so
   // the weights are only ever as far ahead as the activations issued beside them
-  static constexpr int PD = WT == WT_BF16 ? KS_PD_BF16
-                            : WT == WT_FP8  ? (AR == 4 ? KS_PD4_FP8 : KS_PD_FP8)
-                                            : (AR == 4 ? KS_PD4_INT4 : KS_PD_INT4);
+  static constexpr int PD = WT == WT_BF16 ? kPdBf16
+                            : WT == WT_FP8  ? (AR == 4 ? kPd4Fp8 : kPdFp8)
+                                            : (AR == 4 ? kPd4Int4 : kPdInt4);
   static constexpr int NB = kNF * (RAW + NQ);                            // weight loads per wave per step
 };
 
@@ -218,14 +207,14 @@ __device__ __forceinline__ void tile_epilogue(const KsplitParams& p, const TileR
 // rows: fragment row r reads staged row r & 3, so rows 4-15 of the MFMA repeat
 // rows 0-3 and are never stored)
 template <bool GATED, int WT, int AR>
-__global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_kernel(KsplitParams p) {
+__global__ __launch_bounds__(256, kOcc) void gemm_ksplit_kernel(KsplitParams p) {
   using CD = Codec<WT, AR>;
   constexpr int PD = CD::PD, R = PD + 1, NB = CD::NB;
   constexpr int NST = PD + 1;  // activation stages per wave
   constexpr int kASTAGE = AR * kAROW;   // bytes per stage
   constexpr int kAINS = kASTAGE / 1024; // 1 KB direct-to-LDS loads per wave per step
   static_assert(PD >= 2 && (PD - 1) * (NB + kAINS) <= 63, "vmcnt holds at most 63 loads");
-  static_assert(4 * NST * kASTAGE * KS_OCC <= 160 * 1024, "LDS of the resident blocks");
+  static_assert(4 * NST * kASTAGE * kOcc <= 160 * 1024, "LDS of the resident blocks");
   static_assert(4 * NST * kASTAGE >= 4 * kNF * 4 * 64 * 4, "the partial sums meet in the stage memory");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * NST * kASTAGE];
 
@@ -418,7 +407,7 @@ __device__ __forceinline__ TileRef map_tile_scalar(int L, int n_tiles, int group
 }
 
 template <bool GATED, int WT, int PD>
-__global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitParams p) {
+__global__ __launch_bounds__(256, kOcc) void gemm_ksplit_pipe_kernel(KsplitParams p) {
   static_assert(WT == WT_INT4 || WT == WT_FP8, "INT4 or fp8 weights");
   constexpr int AR = 4;
   using CD = Codec<WT, AR>;
@@ -432,7 +421,7 @@ __global__ __launch_bounds__(256, KS_OCC) void gemm_ksplit_pipe_kernel(KsplitPar
   static_assert(kASTAGE == 1024, "one activation load per step");
   static_assert(R <= 4, "a chunk's group words: one per lane group");
   static_assert(PD >= 2 && (PD - 1) * NS + NQ <= 63, "vmcnt holds at most 63 loads");
-  static_assert(KS_OCC * (4 * R * kASTAGE + kRED) <= 160 * 1024, "LDS of the resident blocks");
+  static_assert(kOcc * (4 * R * kASTAGE + kRED) <= 160 * 1024, "LDS of the resident blocks");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[4 * R * kASTAGE + kRED];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -609,7 +598,7 @@ moe_status launch_gemm_ksplit(const GemmLaunch& a, const int32_t* goff, const in
   KsplitParams p{a.A, a.B0, a.B1, a.S0, a.S1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gather};
   p.n_tiles = a.gated ? a.N / 32 : a.N / 64;
   const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles;
-  int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count() * KS_OCC);
+  int64_t grid = std::min<int64_t>(upper, (int64_t)device_cu_count() * kOcc);
   grid = ceil_div(grid, 8) * 8;  // the XCD mapping wants a multiple of 8
   if (grid <= 0) return MOE_OK;
   const int wt = a.w_dtype == MOE_FP8_E4M3FN ? WT_FP8 : a.w_dtype == MOE_INT4 ? WT_INT4 : WT_BF16;

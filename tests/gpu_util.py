@@ -8,8 +8,15 @@ Metrics
     selection gap is below 1e-5 are set aside for the index-set comparison,
     and those whose order gap is below 1e-5 for the order comparison; both
     are counted and reported)
-  layer output     : max |out_gpu - out_ora| / RMS(out_ora)
-                     <= 2e-2 (bf16 weights), 6e-2 (fp8 and INT4 weights), 1e-4 (fp32)
+  layer output     : max |out_gpu - out_ora| / RMS(out_ora over the served tokens)
+                     <= 2e-2 (bf16 and INT4 weights), 6e-2 (fp8 weights), 1e-4 (fp32)
+    The RMS is taken over the rows the oracle gives a nonzero output (tokens
+    that keep at least one expert, or every token with a shared expert): the
+    all-zero rows of fully dropped tokens would otherwise shrink the base and
+    inflate the metric.  The maximum runs over every element, zero rows included.
+    INT4 takes the bf16 bound: its products are exact (bf16 activations times
+    the bf16 numbers 128 + q, f32 sums, the group scale applied once per step),
+    so its error, like the bf16 path's, comes from rounding h to bf16.
 """
 from __future__ import annotations
 
@@ -23,7 +30,7 @@ from oracle import moe_oracle as O
 NEAR_TIE = 1e-5
 TOL_Z = 1e-5
 TOL_W = 1e-5
-TOL_OUT = {W.DT_BF16: 2e-2, W.DT_FP8: 6e-2, W.DT_INT4: 6e-2, W.DT_F32: 1e-4}
+TOL_OUT = {W.DT_BF16: 2e-2, W.DT_FP8: 6e-2, W.DT_INT4: 2e-2, W.DT_F32: 1e-4}
 
 
 def L():
@@ -46,13 +53,41 @@ def rel_err_scaled(got, ref) -> float:
     return float(np.max(np.abs(got - ref) / denom))
 
 
+def served_rms(ref) -> float:
+    """RMS of the reference over its rows that are not all zero (all rows if none is)."""
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return 0.0
+    if ref.ndim == 2:
+        served = np.any(ref != 0.0, axis=1)
+        if served.any():
+            ref = ref[served]
+    return float(np.sqrt(np.mean(ref ** 2)))
+
+
 def out_err(got, ref) -> float:
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     if ref.size == 0:
         return 0.0
-    rms = float(np.sqrt(np.mean(ref ** 2)))
+    rms = served_rms(ref)
     return float(np.max(np.abs(got - ref))) / (rms if rms > 0 else 1.0)
+
+
+def oracle_out_on_routing(inp: W.MoEInputs, g: dict, P) -> np.ndarray:
+    """The oracle's layer output (float64, every element) for the routing the
+    GPU took: its permutation P (checked bit-exact against the GPU's before
+    this is called) and its gate weights.  Experts are copied to the host one
+    at a time; products are float64 BLAS."""
+    x = to_np(inp.x)
+    n = int(P.offsets[-1])
+    y = O.expert_outputs(x[P.src_token[:n]].astype(np.float64), P.offsets, FI.expert_weights(inp, experts="lazy"))
+    y_sh = None
+    shared = FI.shared_weights(inp)
+    if shared is not None:
+        wg, wu, wd = shared.expert(0)
+        y_sh = O.swiglu_ffn(x.astype(np.float64), wg, wu, wd)
+    return O.combine(y, P.dest_row, g["topk_w"], y_sh)
 
 
 def to_np(t):
