@@ -244,6 +244,30 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
                        const moe_routing_out* routing, void* ws, size_t ws_bytes,
                        void* stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, results and errors as moe_forward
+ * (bit-identical output), with the intermediates in a scratch array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library's code object holds on every
+ * device it is loaded on, until the process ends.  Nothing is allocated or
+ * freed: the array's address is looked up once per device (the first call with
+ * that device current) and reused.
+ *   Limit: a layer whose moe_workspace_bytes exceeds MOE_NOALLOC_SCRATCH_BYTES
+ *   is rejected with MOE_ERR_UNSUPPORTED before anything is launched (64 MiB
+ *   covers decode and small batches: e.g. a Mixtral-shaped layer up to T = 256,
+ *   the 256-expert fine-grained layer up to T = 128).
+ *   Concurrency: every call on one device uses that device's one array, and the
+ *   kernels need it from the first launch to the last; calls whose work
+ *   overlaps on one device (other streams, other host threads) race and give
+ *   wrong results.  Serialise them, or use moe_forward with one workspace each.
+ *   The array keeps the last call's contents; no kernel relies on its initial
+ *   contents. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const float* w_router,
+                               const float* bias, const float* gumbel_u,
+                               const moe_expert_weights* weights, void* out, int32_t* stats,
+                               const moe_routing_out* routing, void* stream);
+
 /* ---- load balancing after a routed batch ----
  * Mean router probability and the auxiliary-loss term ([P3] s4.3 training
  * stability: aux = sum_e mean_t(router_probs[t,e]) * expert_count[e]).  The

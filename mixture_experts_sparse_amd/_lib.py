@@ -17,13 +17,14 @@ from . import workloads as W
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_mi355x.so")
 
 MOE_OK = 0
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20  # the per-device scratch of moe_forward_noalloc
 STATUS_NAMES = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
                 3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
 
 # every symbol include/moe.h declares
 EXPORTED = ["moe_status_string", "moe_last_error", "moe_version", "moe_workspace_bytes",
             "moe_permuted_rows", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-            "moe_forward", "moe_router_stats", "moe_bias_update", "moe_profile_enable",
+            "moe_forward", "moe_forward_noalloc", "moe_router_stats", "moe_bias_update", "moe_profile_enable",
             "moe_profile_read"]
 
 
@@ -77,6 +78,8 @@ def _load() -> ctypes.CDLL:
         "moe_combine": ([cfgp, P, P, P, P, P, P], ctypes.c_int),
         "moe_forward": ([cfgp, P, P, P, P, ctypes.POINTER(moe_expert_weights), P, P,
                          ctypes.POINTER(moe_routing_out), P, ctypes.c_size_t, P], ctypes.c_int),
+        "moe_forward_noalloc": ([cfgp, P, P, P, P, ctypes.POINTER(moe_expert_weights), P, P,
+                                 ctypes.POINTER(moe_routing_out), P], ctypes.c_int),
         "moe_router_stats": ([cfgp, P, P, P, P, P, P, P, ctypes.c_size_t, P], ctypes.c_int),
         "moe_bias_update": ([cfgp, P, P, ctypes.c_float, ctypes.c_float, P], ctypes.c_int),
         "moe_profile_enable": ([ctypes.c_int32], ctypes.c_int),
@@ -187,6 +190,19 @@ def moe_forward(cfg, x, w_router, bias, gumbel_u, weights: moe_expert_weights, o
                             ctypes.byref(weights), _ptr(out), _ptr(stats),
                             ctypes.byref(r) if r is not None else None, _ptr(ws),
                             ws.numel() if ws is not None else 0, _stream(stream)), "moe_forward")
+
+
+def moe_forward_noalloc(cfg, x, w_router, bias, gumbel_u, weights: moe_expert_weights, out, stats,
+                        routing: Optional[dict] = None, stream=None):
+    """moe_forward with the library's per-device scratch instead of a workspace."""
+    r = None
+    if routing:
+        r = moe_routing_out(*[None if routing.get(k) is None else routing[k].data_ptr()
+                              for k in ("logits", "topk_idx", "topk_w", "dest_row")])
+    _check(_LIB.moe_forward_noalloc(ctypes.byref(cfg), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(gumbel_u),
+                                    ctypes.byref(weights), _ptr(out), _ptr(stats),
+                                    ctypes.byref(r) if r is not None else None, _stream(stream)),
+           "moe_forward_noalloc")
 
 
 def moe_router_stats(cfg, logits, bias, gumbel_u, counts, prob_mean, aux, ws, stream=None):

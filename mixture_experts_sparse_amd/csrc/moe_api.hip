@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -383,6 +384,30 @@ moe_status run_combine(const moe_config* c, const float* y_perm, const float* y_
   return launch_combine(cl, s, perm_rows(c));
 }
 
+// ---- the allocation-free forward's scratch: one array per device, in the
+// library's code object, whose device address is looked up once per device
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];  // per device ordinal: the array's address, or null until looked up
+
+moe_status scratch_address(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return fail(MOE_ERR_UNSUPPORTED, "device ordinal %d: at most 64 devices", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || !p)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(r));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -534,6 +559,25 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
                tiles_in_permute);
   if (st != MOE_OK) return st;
   return run_combine(cfg, y_perm, y_sh, dest, tw, out, w, s);
+}
+
+moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
+                               const float* gumbel_u, const moe_expert_weights* weights, void* out, int32_t* stats,
+                               const moe_routing_out* routing, void* stream) {
+  g_err[0] = 0;
+  moe_status st = check_config(cfg);
+  if (st != MOE_OK) return st;
+  const size_t need = layout_of(cfg).total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+    return fail(MOE_ERR_UNSUPPORTED,
+                "this layer needs %zu bytes of scratch; moe_forward_noalloc holds %zu per device "
+                "(call moe_forward with a workspace instead)",
+                need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MOE_OK) return st;
+  return moe_forward(cfg, x, w_router, bias, gumbel_u, weights, out, stats, routing, ws,
+                     (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 moe_status moe_router_stats(const moe_config* cfg, const float* logits, const float* bias,

@@ -178,3 +178,19 @@ def test_huge_capacity_factor_limits_nothing(L, cf):
     assert L.workspace_bytes(huge) == L.workspace_bytes(unlimited)
     tiny = L.make_config(s.replace(T=1, capacity_factor=cf))
     assert L.permuted_rows(tiny) == s.k
+
+
+def test_noalloc_refuses_before_touching_the_device(L):
+    """A layer whose workspace exceeds the allocation-free entry point's scratch
+    is refused from the sizes alone (no device call: this runs without a GPU)."""
+    lib = L.lib()
+    cfg = _cfg(L)  # the Mixtral-shaped layer: hundreds of MiB of intermediates
+    assert L.workspace_bytes(cfg) > L.MOE_NOALLOC_SCRATCH_BYTES
+    d = ctypes.c_void_p(256)  # never dereferenced
+    w = L.moe_expert_weights(256, 256, 256, None, None, None, None, None, None, None, None, None)
+    st = lib.moe_forward_noalloc(ctypes.byref(cfg), d, d, None, None, ctypes.byref(w), d, None, None, None)
+    assert st == 2  # MOE_ERR_UNSUPPORTED
+    assert b"scratch" in lib.moe_last_error()
+    # an invalid config is reported as such first
+    bad = _cfg(L, k=0)
+    assert lib.moe_forward_noalloc(ctypes.byref(bad), d, d, None, None, ctypes.byref(w), d, None, None, None) == 1
