@@ -27,6 +27,7 @@
 //    a burst and the reads have landed before the barrier or the next step
 //    waits for them.
 #include <algorithm>
+#include <type_traits>
 
 #include "grouped.h"
 
@@ -105,7 +106,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
 
   for (int U = xcd * chunk + jb; U < lend; U += G8) {
     const int part = U / tiles, L = U - part * tiles;
-    const TileRef tr = map_tile(L, p.n_tiles, p.groups, kBM, p.tp, p.goff);
+    const TileRef tr = map_tile_balanced(L, p.n_tiles, p.groups, p.tp, p.goff);
     const int g = tr.g;
     const size_t kofs = (size_t)part * kpart * 2;  // byte offset of this K part
 
@@ -171,17 +172,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + B_INS));  // step 0 has landed
     block_sync();
 
-    if (wm * 128 >= tr.rows) {
-      // every row of this wave is padding (a tile of at most 128 rows): it
-      // skips the fragment reads and MFMAs and only takes its share of the
-      // loads, with the same waits and the same one barrier per step
-      for (int ks = 0; ks < ksteps; ++ks) {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm(B_INS));
-        block_sync();
-#pragma unroll
-        for (int i = 0; i < 8; ++i) load_one(i, i < A_INS ? ks + 2 : ks + 3);
-      }
-    } else {
+    // 16-row groups of this wave's 128 rows that hold rows of the tile, rounded
+    // up to even: the MFMA rows of the others would only multiply padding
+    const int live = min(8, max(0, tr.rows - wm * 128 + 31) / 32 * 2);
     // fragment entry e of a half: weights first (every MFMA row needs all of
     // them), then the activation rows
     auto read_frag = [&](bf16x8_t (&F)[8 + NJ], int e, const uint8_t* sa, const uint8_t* sb, uint32_t af,
@@ -189,49 +182,70 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
       if (e < NJ) F[8 + e] = *(const bf16x8_t*)(sb + bf + e * 2048);
       else F[e - NJ] = *(const bf16x8_t*)(sa + af + (e - NJ) * 2048);
     };
+    // the K loop for NI live groups (NI = 0: the wave only takes its share of the
+    // loads, with the same waits and the same one barrier per step)
+    auto k_loop = [&](auto ni) {
+      constexpr int NI = decltype(ni)::value;
+      if constexpr (NI == 0) {
+        for (int ks = 0; ks < ksteps; ++ks) {
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(B_INS));
+          block_sync();
 #pragma unroll
-    for (int e = 0; e < 8 + NJ; ++e) read_frag(X, e, smem, smem + B_BASE, a_frag0, b_frag0);
-    // nothing may be pending at the loop head (tile lookups leave scalar loads in
-    // flight, which would make the compiler drain the counter there every step)
-    __builtin_amdgcn_s_waitcnt(kLgkm0);
-
-    int bs = 0;  // weight stage of step ks (ks % 3)
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const int bn = bs == 2 ? 0 : bs + 1;
-      const uint8_t* sa = smem + (ks & 1) * A_BYTES;
-      const uint8_t* sb = smem + B_BASE + bs * B_BYTES;
-      const uint8_t* na = smem + ((ks + 1) & 1) * A_BYTES;
-      const uint8_t* nb = smem + B_BASE + bn * B_BYTES;
-      // first half: MFMAs on X, second-half fragments of this step read alongside
+          for (int i = 0; i < 8; ++i) load_one(i, i < A_INS ? ks + 2 : ks + 3);
+        }
+      } else {
+        constexpr int NE = NJ + NI;                  // fragment reads per half
+        constexpr int RPR = (NE + NI - 1) / NI;      // of them per MFMA row
+        constexpr int LPR = (8 + NI - 1) / NI;       // load instructions per MFMA row
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        // the 12 fragment reads of the half go out over the first six MFMA rows,
-        // so they have landed before anything waits for them
+        for (int e = 0; e < NE; ++e) read_frag(X, e, smem, smem + B_BASE, a_frag0, b_frag0);
+        // nothing may be pending at the loop head (tile lookups leave scalar loads in
+        // flight, which would make the compiler drain the counter there every step)
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        int bs = 0;  // weight stage of step ks (ks % 3)
+        for (int ks = 0; ks < ksteps; ++ks) {
+          const int bn = bs == 2 ? 0 : bs + 1;
+          const uint8_t* sa = smem + (ks & 1) * A_BYTES;
+          const uint8_t* sb = smem + B_BASE + bs * B_BYTES;
+          const uint8_t* na = smem + ((ks + 1) & 1) * A_BYTES;
+          const uint8_t* nb = smem + B_BASE + bn * B_BYTES;
+          // first half: MFMAs on X, second-half fragments of this step read alongside
 #pragma unroll
-        for (int e = 2 * i; e < 2 * i + 2 && e < 8 + NJ; ++e) read_frag(Y, e, sa, sb, a_frag1, b_frag1);
+          for (int i = 0; i < NI; ++i) {
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[i], X[8 + j], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int e = RPR * i; e < RPR * i + RPR && e < NE; ++e) read_frag(Y, e, sa, sb, a_frag1, b_frag1);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[i], X[8 + j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          // step ks + 1 has landed; only the weights of step ks + 2 may still be in flight
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(B_INS));
+          __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's reads of step ks are done
+          block_sync();
+          // second half: MFMAs on Y; the activations of step ks + 2 and the weights of
+          // step ks + 3 requested into the stages step ks has released, and the
+          // first-half fragments of step ks + 1 read, spread over the MFMA rows
+#pragma unroll
+          for (int i = 0; i < NI; ++i) {
+#pragma unroll
+            for (int q = LPR * i; q < LPR * i + LPR && q < 8; ++q) load_one(q, q < A_INS ? ks + 2 : ks + 3);
+#pragma unroll
+            for (int e = RPR * i; e < RPR * i + RPR && e < NE; ++e) read_frag(X, e, na, nb, a_frag0, b_frag0);
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[i], Y[8 + j], acc[i][j]);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          __builtin_amdgcn_s_waitcnt(kLgkm0);  // next step's first-half fragments are in
+          bs = bn;
+        }
       }
-      // step ks + 1 has landed; only the weights of step ks + 2 may still be in flight
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(B_INS));
-      __builtin_amdgcn_s_waitcnt(kLgkm0);  // this wave's reads of step ks are done
-      block_sync();
-      // second half: MFMAs on Y; the activations of step ks + 2 and the weights of
-      // step ks + 3 requested into the stages step ks has released, and the
-      // first-half fragments of step ks + 1 read, one of each per MFMA row
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        load_one(i, i < A_INS ? ks + 2 : ks + 3);
-#pragma unroll
-        for (int e = 2 * i; e < 2 * i + 2 && e < 8 + NJ; ++e) read_frag(X, e, na, nb, a_frag0, b_frag0);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[i], Y[8 + j], acc[i][j]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_waitcnt(kLgkm0);  // next step's first-half fragments are in
-      bs = bn;
-    }
+    };
+    switch (live) {
+      case 8: k_loop(std::integral_constant<int, 8>{}); break;
+      case 6: k_loop(std::integral_constant<int, 6>{}); break;
+      case 4: k_loop(std::integral_constant<int, 4>{}); break;
+      case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      default: k_loop(std::integral_constant<int, 0>{}); break;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this unit
 

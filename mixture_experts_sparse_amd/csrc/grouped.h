@@ -29,6 +29,27 @@ __device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int 
   return r;
 }
 
+// The same walk with the group's rows spread evenly over its m-tiles: a group
+// of c rows in mt = ceil(c / bm) tiles gives tile mi the rows
+// [c mi / mt, c (mi + 1) / mt), so tile heights differ by at most one and no
+// tile is a sliver of a few rows (a sliver costs nearly a whole tile's loads).
+__device__ __forceinline__ TileRef map_tile_balanced(int L, int n_tiles, int groups,
+                                                     const int32_t* __restrict__ tp,
+                                                     const int32_t* __restrict__ goff) {
+  const int g = tp[groups + 1 + L / n_tiles];
+  const int mt = tp[g + 1] - tp[g];
+  const int local = L - tp[g] * n_tiles;
+  const int nt = local / mt, mi = local % mt;
+  const int c = goff[g + 1] - goff[g];
+  const int a = (int)(((int64_t)c * mi) / mt), b = (int)(((int64_t)c * (mi + 1)) / mt);
+  TileRef r;
+  r.g = g;
+  r.nt = nt;
+  r.row0 = goff[g] + a;
+  r.rows = b - a;
+  return r;
+}
+
 // bf16 large-tile grouped GEMM (gemm_big.hip): block tile 256 x 256, 8 waves of 128 x 64
 moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s);
 
