@@ -136,6 +136,7 @@ struct PermuteLaunch {
   int32_t* reroute = nullptr;  // workspace of reroute_ws_ints(T, k, E, fb) (fb > 0 with a limit)
   int32_t* tiles = nullptr;  // or: also write the grouped GEMM's tile lists for tile height
   int tile_bm = 0;           // tile_bm (layout of GemmLaunch::tile_prefix; not with re-routing)
+  int32_t* sk_zero = nullptr;  // with tiles: kSkUnits stream-K counters to clear
 };
 moe_status launch_permute(const PermuteLaunch& a, hipStream_t s);
 
@@ -191,11 +192,19 @@ struct GemmLaunch {
   int64_t group_rows_max = -1;  // most rows any group can hold (the capacity), or -1: unknown
   bool tiles_ready = false; // tile_prefix already holds this launch's tile lists (same
                             // offsets, groups, max_rows and tile height as a previous launch)
+  // stream-K tail of the large-tile kernel: per-unit partial slots (one
+  // 256 x 256 f32 tile per CU, at most kSkUnits) and one arrival counter per
+  // tail tile (kSkUnits ints; zero between launches: the tile-list writers
+  // clear them and the last part of each tile puts its counter back to zero)
+  float* sk_part = nullptr;
+  int32_t* sk_cnt = nullptr;
   int split_k = 1;          // down pass: K split into parts; part 0 goes to `out`,
   float* split_rest = nullptr;  // part p >= 1 to split_rest + (p - 1) * split_stride
   size_t split_stride = 0;  // elements
 };
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
+// most stream-K units of one large-tile launch (units run one per CU)
+constexpr int kSkUnits = 1024;
 // rows per tile of the kernel launch_grouped_gemm picks for `a`
 int grouped_gemm_bm(const GemmLaunch& a);
 // int32 entries of GemmLaunch::tile_prefix for `groups` groups of at most `max_rows` rows in all

@@ -37,8 +37,11 @@ namespace {
 __global__ __launch_bounds__(512) void tiles_kernel(const int32_t* __restrict__ offsets, int groups,
                                                     int single_rows, int64_t max_rows, int bm,
                                                     int32_t* __restrict__ goff,
-                                                    int32_t* __restrict__ tile_prefix) {
+                                                    int32_t* __restrict__ tile_prefix,
+                                                    int32_t* __restrict__ sk_zero) {
   __shared__ int o[512];
+  if (sk_zero)  // the large-tile GEMM's stream-K counters start at zero
+    for (int j = threadIdx.x; j < kSkUnits; j += 512) sk_zero[j] = 0;
   __shared__ int tp[512];
   const int i = threadIdx.x;
   int v = 0;
@@ -359,31 +362,10 @@ static bool use_big(const GemmLaunch& a) {
   return a.gated ? (a.N % 128 == 0) : (a.N % 256 == 0);
 }
 
-int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype) {
-  GemmLaunch probe{};
-  probe.w_dtype = w_dtype;
-  probe.K = K;
-  probe.N = N;
-  probe.gated = false;
-  probe.max_rows = rows;
-  probe.groups = groups;
-  if (!use_big(probe) || rows <= 0) return 1;
-  // expected work units: m-tiles (with about half a ragged tile per busy group) x n-tiles x split
-  const int64_t mt = ceil_div(rows, 256);
-  const int64_t est = (mt + std::min<int64_t>(groups, mt) / 2) * (N / 256);
-  const int cus = device_cu_count();
-  // each extra part costs one more f32 write + read of every row, so a split
-  // must raise the share of CU-rounds doing work by 15 % to be taken
-  int best = 1;
-  double best_eff = 0.0;
-  for (int sk = 1; sk <= 3; ++sk) {
-    if (K % sk || (K / sk) % 64 || K / sk < 512) continue;
-    const int64_t units = est * sk;
-    const double eff = (double)units / (double)(ceil_div(units, cus) * cus);
-    if (eff > best_eff * 1.15) { best = sk; best_eff = eff; }
-  }
-  return best;
-}
+// No pass is split into K parts for the combine to add: the large-tile kernel
+// balances its last round with a stream-K split it resolves itself, so every
+// pass writes complete rows of y.
+int down_split_k(int64_t, int, int, int, int) { return 1; }
 
 // y[r] += rest parts, for valid rows; one block per 4 rows, float4 lanes
 __global__ __launch_bounds__(256) void sum_partials_kernel(float4* __restrict__ y, const float4* __restrict__ rest,
@@ -438,7 +420,7 @@ moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s) {
   if (!a.tiles_ready) {
     tok = begin_launch("gemm_tiles", s);
     hipLaunchKernelGGL(tiles_kernel, dim3(1), dim3(512), 0, s, a.offsets, a.groups, a.single_rows,
-                       a.max_rows, bm, goff, tp);
+                       a.max_rows, bm, goff, tp, a.sk_cnt);
     st = end_launch(tok, s);
     if (st != MOE_OK) return st;
   }

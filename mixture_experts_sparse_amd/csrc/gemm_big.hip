@@ -62,11 +62,13 @@ struct BigParams {
   const int32_t* goff;
   const int32_t* tp;
   int groups, K, N, n_tiles;
-  int split;             // K split into this many parts (down pass only)
-  float* split_rest;     // part p >= 1 goes to split_rest + (p - 1) * split_stride
-  size_t split_stride;
   const int32_t* gather; // A row r is A[gather[r]], or null
+  int G;                 // stream-K: units of the tail round (one per CU), <= kSkUnits
+  float* sk_part;        // G partial slots of 64 Ki floats (one per tail unit), or null: no stream-K
+  int32_t* sk_cnt;       // arrival counter per tail tile (zero between launches)
 };
+
+constexpr int kMinSkSteps = 16;  // K steps of the shortest stream-K fragment
 
 // Waves: 2 along M (128 rows each) x 4 along N (64 weight rows each).
 template <bool GATED>
@@ -87,12 +89,25 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, kept scalar
   const int wm = w / WAVES_N, wn = w % WAVES_N;
   const int K = p.K, N = p.N;
-  const int kpart = K / p.split, ksteps = kpart / kBK;
-  const int tiles = p.n_tiles * p.tp[p.groups];
-  const int total = tiles * p.split;  // work units: (K part, tile), K part major
+  const int KS = K / kBK;                              // K steps of a whole tile
+  const int n_total = p.n_tiles * p.tp[p.groups];
+  // Work units.  Whole tiles (D of them) each make one unit, except that the
+  // last R = n_total mod G tiles -- a partial last round -- are cut along K
+  // into P parts each (stream-K), P = min(G / R, KS / kMinSkSteps) when that is
+  // at least 2: unit D + u is part u % P of tail tile u / P, K steps
+  // [KS q / P, KS (q + 1) / P), q = u % P.  Each XCD takes a contiguous share of
+  // the whole tiles and then of the tail units, so the parts of one tail tile
+  // mostly run on one XCD.
+  int R = 0, P = 0;
+  if (p.sk_part) {
+    R = n_total % p.G;
+    P = R ? min(p.G / R, KS / kMinSkSteps) : 0;
+    if (P < 2) R = P = 0;
+  }
+  const int D = n_total - R, NU = R * P;
   const int G8 = gridDim.x >> 3, xcd = blockIdx.x & 7, jb = blockIdx.x >> 3;
-  const int chunk = (total + 7) >> 3;
-  const int lend = min(total, (xcd + 1) * chunk);
+  const int dp0 = (int)((int64_t)D * xcd / 8), n_dp = (int)((int64_t)D * (xcd + 1) / 8) - dp0;
+  const int sk0 = NU * xcd / 8, n_x = n_dp + NU * (xcd + 1) / 8 - sk0;
 
   // per-lane constants of the swizzled layout
   const int dma_row = lane >> 3;                  // row inside an 8-row slab
@@ -104,11 +119,23 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
   const uint32_t b_frag0 = (uint32_t)((wn * WN + frow) * kRow + ((kg ^ (frow & 7)) * 16));
   const uint32_t b_frag1 = (uint32_t)((wn * WN + frow) * kRow + (((kg + 4) ^ (frow & 7)) * 16));
 
-  for (int U = xcd * chunk + jb; U < lend; U += G8) {
-    const int part = U / tiles, L = U - part * tiles;
+  for (int local = jb; local < n_x; local += G8) {
+    // the unit: tile L, K steps [kbeg, kbeg + ksteps); u = its tail unit, or -1
+    const int u = local < n_dp ? -1 : sk0 + local - n_dp;
+    int L, kbeg, ksteps;
+    if (u < 0) {
+      L = dp0 + local;
+      kbeg = 0;
+      ksteps = KS;
+    } else {
+      const int q = u % P;
+      L = D + u / P;
+      kbeg = KS * q / P;
+      ksteps = KS * (q + 1) / P - kbeg;
+    }
     const TileRef tr = map_tile_balanced(L, p.n_tiles, p.groups, p.tp, p.goff);
     const int g = tr.g;
-    const size_t kofs = (size_t)part * kpart * 2;  // byte offset of this K part
+    const size_t kofs = (size_t)kbeg * kRow;  // byte offset of the fragment's first K step
 
     // load sources: wave-uniform bases plus 32-bit per-lane byte offsets
     // rows past the group's end repeat its last row; with a gather map the rows
@@ -249,6 +276,60 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this unit
 
+    if (u >= 0) {
+      // A part of a tail tile: its partial sums go to the unit's slot with
+      // agent-coherent stores; the last part to arrive (counted by one atomic
+      // per tile) adds the P parts in part order -- the sum does not depend on
+      // which part finishes last -- and runs the epilogue.
+      const int ts = u / P;
+      const size_t lane_base = (size_t)w * (8 * NJ * 4 * 64) + lane;
+      auto slot_at = [&](int unit, int i, int j, int r) {
+        return p.sk_part + ((size_t)unit << 16) + lane_base + (size_t)((i * NJ + j) * 4 + r) * 64;
+      };
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (i < live)
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              __hip_atomic_store(slot_at(u, i, j, r), acc[i][j][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // the stores are done
+      block_sync();
+      if (tid == 0) {
+        const int before = __hip_atomic_fetch_add(p.sk_cnt + ts, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int last = before == P - 1;
+        if (last) __hip_atomic_store(p.sk_cnt + ts, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *(volatile int*)smem = last;
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+      }
+      block_sync();
+      const int last = *(volatile int*)smem;
+      if (!last) continue;  // (the next unit starts with a barrier before it touches LDS)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i >= live) continue;
+        f32x4_t sum[NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) sum[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int q = 0; q < P; ++q) {
+          const int uq = ts * P + q;
+          if (uq == u) {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j) sum[j] += acc[i][j];
+          } else {
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                sum[j][r] += __hip_atomic_load(slot_at(uq, i, j, r), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) acc[i][j] = sum[j];
+      }
+    }
+
     // ---- epilogue (rows past the group's end are not stored)
     const int col_in = lane & 15;
     const int rq = (lane >> 4) * 4;
@@ -283,7 +364,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
           *(uint4*)(h + (size_t)(tr.row0 + wm * 128 + m) * N + f0 + sg * 8) = v;
       }
     } else {
-      float* y = part == 0 ? (float*)p.out : p.split_rest + (size_t)(part - 1) * p.split_stride;
+      float* y = (float*)p.out;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int n = tr.nt * BNR + wn * WN + j * 16 + col_in;
@@ -305,12 +386,19 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
 // 8 waves.  Requires N % (gated ? 128 : 256) == 0 and K % 64 == 0 (per K part);
 // goff / tile prefix already built for 256-row tiles.
 moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const int32_t* tp, hipStream_t s) {
-  BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gated ? 1 : a.split_k,
-              a.split_rest, a.split_stride, a.gather};
+  BigParams p{a.A, a.B0, a.B1, a.out, goff, tp, a.groups, a.K, a.N, 0, a.gather, 0, nullptr, nullptr};
   p.n_tiles = a.gated ? a.N / 128 : a.N / 256;
-  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles * p.split;
-  int64_t grid = ceil_div(upper, 8) * 8;
-  if (grid <= 0) return MOE_OK;
+  // the stream-K tail: at most one unit per CU, each at least kMinSkSteps
+  // long; the counters were cleared with the tile lists
+  if (a.sk_part && a.sk_cnt) {
+    p.G = std::min(device_cu_count(), kSkUnits);
+    p.sk_part = a.sk_part;
+    p.sk_cnt = a.sk_cnt;
+  }
+  // whole tiles plus at most G tail units, spread over the 8 XCDs
+  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles + p.G;
+  int64_t grid = (ceil_div(upper, 8) + 1) * 8;
+  if (upper <= 0) return MOE_OK;
   const char* name = a.shared ? (a.gated ? "shared_gate_up_bf16" : "shared_down_bf16")
                               : (a.gated ? "gemm_gate_up_bf16" : "gemm_down_bf16");
   int tok = begin_launch(name, s);

@@ -165,13 +165,27 @@ int64_t perm_rows(const moe_config* c) {
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 
+// whether a pass of this layer (routed or shared, gate/up or down) runs on the
+// large-tile kernel, whose stream-K tail needs partial slots in the workspace
+bool uses_stream_k(const moe_config* c) {
+  for (int shared = 0; shared <= c->n_shared; ++shared)
+    for (int gated = 0; gated <= 1; ++gated) {
+      GemmLaunch g{};
+      g.w_dtype = c->w_dtype; g.gated = gated != 0;
+      g.K = gated ? c->d : c->F; g.N = gated ? c->F : c->d;
+      g.groups = shared ? 1 : c->E; g.max_rows = shared ? c->T : perm_rows(c);
+      if (grouped_gemm_bm(g) == 256) return true;
+    }
+  return false;
+}
+
 struct Layout {
   // router scratch (bf16 path): split weights, logit partials; overlaps the
   // permute / ffn scratch, which is only used after the router has finished
   int route_ep, route_split;
   size_t route_wt, route_part, route_end;
   // permute / ffn scratch
-  size_t hist, reroute, tiles, tiles_sh, h, h_sh;
+  size_t hist, reroute, tiles, tiles_sh, sk_cnt, sk_part, h, h_sh;
   int split, split_sh;          // K splits of the routed / shared down passes
   size_t y_rest, y_sh_rest;     // partial sums 1.. of y_perm / y_shared
   // forward intermediates
@@ -203,6 +217,10 @@ Layout layout_of(const moe_config* c) {
   L.perm_end = o;
   L.tiles = take(sizeof(int32_t) * tile_list_ints(c->E, R));
   L.tiles_sh = take(sizeof(int32_t) * tile_list_ints(1, c->T));
+  // stream-K tail of the large-tile down passes: counters and partial slots
+  // (reused by the shared expert's passes, which run after the routed ones)
+  L.sk_cnt = take(sizeof(int32_t) * kSkUnits);
+  L.sk_part = take(uses_stream_k(c) ? sizeof(float) * (size_t)std::min(device_cu_count(), kSkUnits) * 65536 : 0);
   L.h = take(hb * R * c->F);
   L.h_sh = take(c->n_shared ? hb * (size_t)c->T * c->F : 0);
   L.split = down_split_k(R, c->E, c->F, c->d, c->w_dtype);
@@ -304,6 +322,7 @@ moe_status run_permute(const moe_config* c, const void* x, const int32_t* topk_i
   p.reroute = (int32_t*)(ws + L.reroute);
   p.tiles = tiles;
   p.tile_bm = tile_bm;
+  p.sk_zero = tiles ? (int32_t*)(ws + L.sk_cnt) : nullptr;
   return launch_permute(p, s);
 }
 
@@ -319,6 +338,8 @@ GemmLaunch gate_up_launch(const moe_config* c, const void* x, const void* x_perm
   g.groups = c->E; g.single_rows = 0; g.max_rows = perm_rows(c); g.K = c->d; g.N = c->F; g.gated = true;
   // with re-routing a group still holds at most C rows
   g.group_rows_max = capacity_of(c) >= 0 ? std::min<int64_t>(capacity_of(c), g.max_rows) : g.max_rows;
+  g.sk_cnt = (int32_t*)(ws + L.sk_cnt);
+  g.sk_part = uses_stream_k(c) ? (float*)(ws + L.sk_part) : nullptr;
   return g;
 }
 

@@ -34,7 +34,9 @@ __device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, int 
 // final per-expert row counts, by the one block that knows them.  Thread e holds
 // expert e's kept rows and exclusive row offset; `scan` is 256 ints of LDS.
 __device__ __forceinline__ void write_tile_lists(int e, int kept, int off_excl, int E, int bm, int* scan,
-                                                 int32_t* __restrict__ tiles) {
+                                                 int32_t* __restrict__ tiles, int32_t* __restrict__ sk_zero) {
+  if (sk_zero)  // the large-tile GEMM's stream-K counters start at zero
+    for (int i = e; i < kSkUnits; i += 256) sk_zero[i] = 0;
   const int nt = (e < E) ? (kept + bm - 1) / bm : 0;
   scan[e] = nt;
   __syncthreads();
@@ -81,7 +83,8 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(int32_t* __restrict__ hi
                                                         int32_t* __restrict__ offsets,
                                                         int32_t* __restrict__ n_dropped,
                                                         int32_t* __restrict__ stats,
-                                                        int32_t* __restrict__ tiles, int tile_bm) {
+                                                        int32_t* __restrict__ tiles, int tile_bm,
+                                                        int32_t* __restrict__ sk_zero) {
   __shared__ int kept_s[256];
   __shared__ int drop_s[256];
   const int e = threadIdx.x;
@@ -119,7 +122,7 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(int32_t* __restrict__ hi
   if (tiles) {
     const int incl = kept_s[e];
     __syncthreads();  // (kept_s is reused as the tile scan)
-    write_tile_lists(e, kept, incl - kept, E, tile_bm, kept_s, tiles);
+    write_tile_lists(e, kept, incl - kept, E, tile_bm, kept_s, tiles, sk_zero);
   }
 }
 
@@ -205,7 +208,8 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __r
                                                               int32_t* __restrict__ stats,
                                                               int32_t* __restrict__ dest_row,
                                                               int32_t* __restrict__ src_token,
-                                                              int32_t* __restrict__ tiles, int tile_bm) {
+                                                              int32_t* __restrict__ tiles, int tile_bm,
+                                                              int32_t* __restrict__ sk_zero) {
   __shared__ int running[256];
   __shared__ int wcnt[4][256];
   __shared__ int kept_s[256];
@@ -247,7 +251,7 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __r
     if (stats) stats[2 * E] = drop_s[255];
   }
   __syncthreads();
-  if (tiles) write_tile_lists(e, kept, kept_s[e] - kept, E, tile_bm, drop_s, tiles);
+  if (tiles) write_tile_lists(e, kept, kept_s[e] - kept, E, tile_bm, drop_s, tiles, sk_zero);
   running[e] = 0;  // ranks start at zero in the only chunk
   __syncthreads();
   const int n_rows = off_s[E];
@@ -728,7 +732,7 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
     tok = begin_launch("permute_count_rank", s);
     hipLaunchKernelGGL(count_rank_kernel, dim3(1), dim3(kThreads), 0, s, a.topk_idx, P, a.E, a.k, ld, a.capacity,
                        a.rows, a.counts, a.offsets, a.n_dropped, a.stats, a.dest_row, a.src_token, tiles,
-                       a.tile_bm);
+                       a.tile_bm, a.sk_zero);
     st = end_launch(tok, s);
     if (st != MOE_OK) return st;
   } else {
@@ -739,7 +743,7 @@ moe_status launch_permute(const PermuteLaunch& a, hipStream_t s) {
 
     tok = begin_launch("permute_scan", s);
     hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kThreads), 0, s, a.hist, nblk, a.E, a.capacity,
-                       a.counts, a.offsets, a.n_dropped, a.stats, tiles, a.tile_bm);
+                       a.counts, a.offsets, a.n_dropped, a.stats, tiles, a.tile_bm, a.sk_zero);
     st = end_launch(tok, s);
     if (st != MOE_OK) return st;
 

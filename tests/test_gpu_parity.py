@@ -83,6 +83,18 @@ SMALL = {
     "k_equals_E_cap": WK["mixtral_bf16"].replace(name="kEc", T=50, d=128, E=64, k=64, F=64,
                                                   capacity_factor=0.5),
     "single_token": WK["mixtral_bf16"].replace(name="one", T=1, d=256, E=8, k=2, F=128),
+    # the large-tile kernel's stream-K tail (a partial last round of tiles cut
+    # along K into P parts, P = min(256 / tail tiles, K steps / 16)): down
+    # passes of 8 tiles in 2 parts, 16 tiles of 40 K steps in parts of 20, 8
+    # tiles in 4 parts; a gate/up pass of 16 tiles in 4 parts; and 280 tiles
+    # per pass = 256 whole ones plus a tail of 24 in 2 parts, gate/up (560 =
+    # 512 + 48) likewise (Zipf-skewed rows per expert)
+    "sk_parts": WK["mixtral_bf16"].replace(name="skp", T=600, d=256, E=8, k=2, F=2048),
+    "sk_K40": WK["mixtral_bf16"].replace(name="sk40", T=700, d=512, E=8, k=2, F=2560),
+    "sk_parts4": WK["mixtral_bf16"].replace(name="skp4", T=600, d=256, E=8, k=2, F=4096),
+    "sk_gate_up4": WK["mixtral_bf16"].replace(name="skg4", T=600, d=4096, E=8, k=2, F=256),
+    "sk_mixed": WK["mixtral_bf16"].replace(name="skm", T=4000, d=2048, E=8, k=2, F=2048,
+                                           bias_mode=W.BIAS_LOGIT, bias_kind="zipf1.2"),
     "f32_ragged": WK["tiny_fp32"].replace(name="f32r", T=203, d=256, E=6, k=2, F=96),
 }
 
