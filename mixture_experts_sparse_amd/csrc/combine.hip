@@ -12,10 +12,12 @@
 // Bandwidth-bound: one wave per token (or, for few tokens, wpt waves per
 // token, each taking every wpt-th stretch of the row, so a decode batch still
 // has hundreds of waves and each makes one or two round trips), 16-byte vector
-// loads of the k source rows (gathered by dest_row), up to four slots' rows in
-// flight at once, f32 FMAs in j order, one store of the row.
-// When the down projection split its reduction, the partial sums of a row are
-// added in part order first, so the result does not depend on scheduling.
+// loads of the k source rows (gathered by dest_row), the rows of one or two
+// slots in flight at once, f32 FMAs in j order, one store of the row.
+// Expert rows are read and output rows written once: both go through
+// non-temporal accesses, which keep them from displacing cache lines other
+// data will use (measured 482 -> 444 us at 8192 tokens x 8 slots x 7168; two
+// slots of eight vectors per lane instead of four of four: 435 us).
 #include <type_traits>
 
 #include "common.h"
@@ -23,20 +25,10 @@
 namespace moe {
 namespace {
 
-struct Parts {
-  const float4* rest;  // parts 1.. of a partial-sum buffer
-  size_t stride4;      // float4s between parts
-  int n;               // number of parts (1 = a plain buffer)
-};
-
-// value of row r, vector v of a buffer that may be split into partial sums
-__device__ __forceinline__ float4 load_parts(const float4* __restrict__ first, const Parts& P, size_t off) {
-  float4 a = first[off];
-  for (int p = 1; p < P.n; ++p) {
-    const float4 b = P.rest[(size_t)(p - 1) * P.stride4 + off];
-    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-  }
-  return a;
+// vector off of a row-major f32 buffer read once (non-temporal)
+__device__ __forceinline__ float4 load_once(const float4* __restrict__ buf, size_t off) {
+  const f32x4_t v = __builtin_nontemporal_load((const f32x4_t*)buf + off);
+  return make_float4(v[0], v[1], v[2], v[3]);
 }
 
 template <bool BF16OUT>
@@ -47,7 +39,8 @@ __device__ __forceinline__ void store_out(void* out, size_t off, const float4& a
     o.y = (uint32_t)f32_to_bf16_rne(acc.z) | ((uint32_t)f32_to_bf16_rne(acc.w) << 16);
     ((uint2*)out)[off] = o;
   } else {
-    ((float4*)out)[off] = acc;
+    const f32x4_t v = {acc.x, acc.y, acc.z, acc.w};
+    __builtin_nontemporal_store(v, (f32x4_t*)out + off);
   }
 }
 
@@ -61,7 +54,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ topk_w,
                                                       void* __restrict__ out, int T, int vec_per_row,
-                                                      int k, int64_t rows, Parts yp, Parts sp, int wpt) {
+                                                      int k, int64_t rows, int wpt) {
   const int lane = threadIdx.x & 63;
   const int gw = blockIdx.x * 4 + (threadIdx.x >> 6);  // global wave
   const int t = gw / wpt, part = gw - t * wpt;
@@ -86,7 +79,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
         for (int u = 0; u < U; ++u) {
           const int v = v0 + 64 * u;
           y[jj][u] = (row[jj] >= 0 && v < vec_per_row)
-                         ? load_parts(y_perm, yp, (size_t)row[jj] * vec_per_row + v) : make_float4(0, 0, 0, 0);
+                         ? load_once(y_perm, (size_t)row[jj] * vec_per_row + v) : make_float4(0, 0, 0, 0);
         }
       }
 #pragma unroll
@@ -106,7 +99,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
       for (int u = 0; u < U; ++u) {
         const int v = v0 + 64 * u;
         if (v < vec_per_row) {
-          const float4 s = load_parts(y_shared, sp, (size_t)t * vec_per_row + v);
+          const float4 s = load_once(y_shared, (size_t)t * vec_per_row + v);
           acc[u].x += s.x; acc[u].y += s.y; acc[u].z += s.z; acc[u].w += s.w;
         }
       }
@@ -124,32 +117,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const float4* __restrict__
 moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows) {
   if (a.T == 0) return MOE_OK;
   const int vec = a.d / 4;
+  // slots requested together: one at a time for k <= 2 at full occupancy (the
+  // extra registers would cost waves), else two slots of eight vectors per lane;
+  // with few tokens, four slots of four vectors
+  const bool one = a.k <= 2 && (int64_t)a.T * 2 > 512;
+  const bool few = !one && (int64_t)a.T * 2 <= 512;
+  const int U = few || one ? 4 : 8;
   // waves per token: enough that a small batch fills the chip (about 512 waves),
   // never more than the row's trips
-  const int trips = (int)ceil_div(vec, 64 * 4);
+  const int trips = (int)ceil_div(vec, 64 * U);
   int wpt = 1;
   while (wpt * 2 <= trips && (int64_t)a.T * wpt * 2 <= 512) wpt *= 2;
   const dim3 grid((unsigned)ceil_div((int64_t)a.T * wpt, 4));
-  const Parts yp{(const float4*)a.y_rest, a.y_stride / 4, a.y_split};
-  const Parts sp{(const float4*)a.sh_rest, a.sh_stride / 4, a.sh_split};
   int tok = begin_launch("combine", s);
-  // slots requested together: four at a time when a token has many, or when a
-  // small batch leaves registers to spare (measured: one at a time is faster for
-  // k <= 2 at full occupancy, where the extra registers cost waves)
-  auto go = [&](auto bf16_tag, auto jb_tag) {
+  auto go = [&](auto bf16_tag, auto u_tag, auto jb_tag) {
     constexpr bool B = decltype(bf16_tag)::value;
-    constexpr int JB = decltype(jb_tag)::value;
-    hipLaunchKernelGGL((combine_kernel<B, 4, JB>), grid, dim3(256), 0, s, (const float4*)a.y_perm,
-                       (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec, a.k, rows, yp, sp, wpt);
+    hipLaunchKernelGGL((combine_kernel<B, decltype(u_tag)::value, decltype(jb_tag)::value>), grid, dim3(256), 0, s,
+                       (const float4*)a.y_perm, (const float4*)a.y_shared, a.dest_row, a.topk_w, a.out, a.T, vec,
+                       a.k, rows, wpt);
   };
   using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
   using I4 = std::integral_constant<int, 4>;
-  const bool one = a.k <= 2 && wpt == 1;
-  if (a.out_dtype == MOE_BF16) {
-    if (one) go(std::true_type{}, I1{}); else go(std::true_type{}, I4{});
-  } else {
-    if (one) go(std::false_type{}, I1{}); else go(std::false_type{}, I4{});
-  }
+  using I8 = std::integral_constant<int, 8>;
+  auto pick = [&](auto bf16_tag) {
+    if (one) go(bf16_tag, I4{}, I1{});
+    else if (few) go(bf16_tag, I4{}, I4{});
+    else go(bf16_tag, I8{}, I2{});
+  };
+  if (a.out_dtype == MOE_BF16) pick(std::true_type{});
+  else pick(std::false_type{});
   return end_launch(tok, s);
 }
 

@@ -158,14 +158,6 @@ moe_status launch_bias_update(const int32_t* counts, float* bias, int E, float d
 struct CombineLaunch {
   const float* y_perm; const float* y_shared; const int32_t* dest_row; const float* topk_w;
   void* out; int T, d, k, out_dtype;
-  // y_perm may be the first of y_split partial sums, the others at
-  // y_rest + (p - 1) * y_stride; they are added in order before weighting.
-  int y_split = 1;
-  const float* y_rest = nullptr;
-  size_t y_stride = 0;
-  int sh_split = 1;           // the same for y_shared
-  const float* sh_rest = nullptr;
-  size_t sh_stride = 0;
 };
 // rows: size of y_perm; destinations outside [0, rows) are ignored
 moe_status launch_combine(const CombineLaunch& a, hipStream_t s, int64_t rows);
@@ -201,9 +193,6 @@ struct GemmLaunch {
   // clear them and the last part of each tile puts its counter back to zero)
   float* sk_part = nullptr;
   int32_t* sk_cnt = nullptr;
-  int split_k = 1;          // down pass: K split into parts; part 0 goes to `out`,
-  float* split_rest = nullptr;  // part p >= 1 to split_rest + (p - 1) * split_stride
-  size_t split_stride = 0;  // elements
 };
 moe_status launch_grouped_gemm(const GemmLaunch& a, hipStream_t s);
 // most stream-K units of one large-tile launch (units run one per CU)
@@ -218,13 +207,8 @@ inline int64_t tile_list_ints(int groups, int64_t max_rows) {
 // (row byte offsets into A must also fit 32 bits: A_rows * K * 2 < 2^32)
 bool gather_ok(const GemmLaunch& a, int64_t a_rows);
 
-// K-split chosen for a down pass of `rows` rows (1 = no split); the large-tile
-// kernel is the only one that splits.  Deterministic function of the shape.
-int down_split_k(int64_t rows, int groups, int K, int N, int w_dtype);
 
-// y[r] += sum_{p = 1 .. split-1} rest[(p-1) * stride + r] for the rows r < offsets[groups]
-// (or < rows when offsets is null), in partial order.
-moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int split,
-                               const int32_t* offsets, int groups, int64_t rows, int d, hipStream_t s);
+
+
 
 }  // namespace moe

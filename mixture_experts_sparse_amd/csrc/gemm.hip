@@ -362,38 +362,6 @@ static bool use_big(const GemmLaunch& a) {
   return a.gated ? (a.N % 128 == 0) : (a.N % 256 == 0);
 }
 
-// No pass is split into K parts for the combine to add: the large-tile kernel
-// balances its last round with a stream-K split it resolves itself, so every
-// pass writes complete rows of y.
-int down_split_k(int64_t, int, int, int, int) { return 1; }
-
-// y[r] += rest parts, for valid rows; one block per 4 rows, float4 lanes
-__global__ __launch_bounds__(256) void sum_partials_kernel(float4* __restrict__ y, const float4* __restrict__ rest,
-                                                           size_t stride4, int split,
-                                                           const int32_t* __restrict__ offsets, int groups,
-                                                           int64_t rows, int vec) {
-  const int64_t n = offsets ? (int64_t)min<int64_t>(offsets[groups], rows) : rows;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= n) return;
-  for (int v = threadIdx.x & 63; v < vec; v += 64) {
-    float4 a = y[r * vec + v];
-    for (int p = 1; p < split; ++p) {
-      const float4 b = rest[(size_t)(p - 1) * stride4 + r * vec + v];
-      a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
-    }
-    y[r * vec + v] = a;
-  }
-}
-
-moe_status launch_sum_partials(float* y, const float* rest, size_t stride, int split, const int32_t* offsets,
-                               int groups, int64_t rows, int d, hipStream_t s) {
-  if (split <= 1 || rows <= 0) return MOE_OK;
-  int tok = begin_launch("sum_partials", s);
-  hipLaunchKernelGGL(sum_partials_kernel, dim3((unsigned)ceil_div(rows, 4)), dim3(256), 0, s, (float4*)y,
-                     (const float4*)rest, stride / 4, split, offsets, groups, rows, d / 4);
-  return end_launch(tok, s);
-}
-
 bool gather_ok(const GemmLaunch& a, int64_t a_rows) {
   if (!use_big(a) && !stream_bm(a)) return false;
   return a_rows * (int64_t)a.K * 2 < ((int64_t)1 << 32);

@@ -186,8 +186,6 @@ struct Layout {
   size_t route_wt, route_part, route_end;
   // permute / ffn scratch
   size_t hist, reroute, tiles, tiles_sh, sk_cnt, sk_part, h, h_sh;
-  int split, split_sh;          // K splits of the routed / shared down passes
-  size_t y_rest, y_sh_rest;     // partial sums 1.. of y_perm / y_shared
   // forward intermediates
   size_t logits, idx, w, counts, offsets, dest, src, ndrop, x_perm, y_perm, y_sh;
   size_t perm_end, ffn_end, total;
@@ -223,10 +221,6 @@ Layout layout_of(const moe_config* c) {
   L.sk_part = take(uses_stream_k(c) ? sizeof(float) * (size_t)std::min(device_cu_count(), kSkUnits) * 65536 : 0);
   L.h = take(hb * R * c->F);
   L.h_sh = take(c->n_shared ? hb * (size_t)c->T * c->F : 0);
-  L.split = down_split_k(R, c->E, c->F, c->d, c->w_dtype);
-  L.split_sh = c->n_shared ? down_split_k(c->T, 1, c->F, c->d, c->w_dtype) : 1;
-  L.y_rest = take(sizeof(float) * (size_t)(L.split - 1) * R * c->d);
-  L.y_sh_rest = take(sizeof(float) * (size_t)(L.split_sh - 1) * c->T * c->d);
   L.ffn_end = o;
   o = std::max(L.ffn_end, L.route_end);
   L.logits = take(sizeof(float) * (size_t)c->T * c->E);
@@ -343,16 +337,13 @@ GemmLaunch gate_up_launch(const moe_config* c, const void* x, const void* x_perm
   return g;
 }
 
-// reduce_partials: fold the down pass's K-split partial sums into y_perm / y_shared
-// (the standalone entry point); moe_forward leaves them for the combine to add.
 // gather: src_token when the gate/up pass reads x directly (x_perm is then unused).
 // tiles_ready: the permute already wrote the gate/up pass's tile lists
 moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const int32_t* gather,
                    const int32_t* offsets, const moe_expert_weights* w, float* y_perm, float* y_shared, char* ws,
-                   bool reduce_partials, hipStream_t s, bool tiles_ready = false) {
+                   hipStream_t s, bool tiles_ready = false) {
   if (c->T == 0) return MOE_OK;
   const Layout L = layout_of(c);
-  const int64_t R = perm_rows(c);
   // routed experts: gate/up pass then down pass
   GemmLaunch g = gate_up_launch(c, x, x_perm, gather, offsets, w, ws);
   g.tiles_ready = tiles_ready;
@@ -361,47 +352,27 @@ moe_status run_ffn(const moe_config* c, const void* x, const void* x_perm, const
   const int bm_gate_up = grouped_gemm_bm(g);
   g.A = ws + L.h; g.gather = nullptr; g.B0 = w->w_down; g.B1 = nullptr; g.S0 = w->s_down; g.S1 = nullptr;
   g.out = y_perm; g.K = c->F; g.N = c->d; g.gated = false;
-  g.split_k = L.split; g.split_rest = (float*)(ws + L.y_rest); g.split_stride = (size_t)R * c->d;
   g.tiles_ready = grouped_gemm_bm(g) == bm_gate_up;  // same offsets and rows: reuse the tile lists
   st = launch_grouped_gemm(g, s);
-  if (st == MOE_OK && reduce_partials)
-    st = launch_sum_partials(y_perm, (const float*)(ws + L.y_rest), (size_t)R * c->d, L.split, offsets, c->E, R,
-                             c->d, s);
   if (st != MOE_OK || !c->n_shared) return st;
   // shared expert over all tokens
   g.A = x; g.B0 = w->sh_gate; g.B1 = w->sh_up; g.S0 = w->sh_s_gate; g.S1 = w->sh_s_up;
   g.out = ws + L.h_sh; g.offsets = nullptr; g.tile_prefix = (int32_t*)(ws + L.tiles_sh);
   g.groups = 1; g.single_rows = c->T; g.max_rows = c->T; g.K = c->d; g.N = c->F; g.gated = true;
-  g.shared = true; g.tiles_ready = false; g.split_k = 1; g.group_rows_max = c->T;
+  g.shared = true; g.tiles_ready = false; g.group_rows_max = c->T;
   st = launch_grouped_gemm(g, s);
   if (st != MOE_OK) return st;
   const int bm_sh = grouped_gemm_bm(g);
   g.A = ws + L.h_sh; g.B0 = w->sh_down; g.B1 = nullptr; g.S0 = w->sh_s_down; g.S1 = nullptr;
   g.out = y_shared; g.K = c->F; g.N = c->d; g.gated = false;
   g.tiles_ready = grouped_gemm_bm(g) == bm_sh;
-  g.split_k = L.split_sh; g.split_rest = (float*)(ws + L.y_sh_rest); g.split_stride = (size_t)c->T * c->d;
-  st = launch_grouped_gemm(g, s);
-  if (st == MOE_OK && reduce_partials)
-    st = launch_sum_partials(y_shared, (const float*)(ws + L.y_sh_rest), (size_t)c->T * c->d, L.split_sh, nullptr,
-                             1, c->T, c->d, s);
-  return st;
+  return launch_grouped_gemm(g, s);
 }
 
-// ws_parts: the workspace holding K-split partial sums of y_perm / y_shared (moe_forward), or null
 moe_status run_combine(const moe_config* c, const float* y_perm, const float* y_shared,
-                       const int32_t* dest_row, const float* topk_w, void* out, const char* ws_parts,
-                       hipStream_t s) {
-  CombineLaunch cl{y_perm, c->n_shared ? y_shared : nullptr, dest_row, topk_w, out, c->T, c->d, c->top_k,
-                   c->out_dtype};
-  if (ws_parts) {
-    const Layout L = layout_of(c);
-    cl.y_split = L.split;
-    cl.y_rest = (const float*)(ws_parts + L.y_rest);
-    cl.y_stride = (size_t)perm_rows(c) * c->d;
-    cl.sh_split = L.split_sh;
-    cl.sh_rest = (const float*)(ws_parts + L.y_sh_rest);
-    cl.sh_stride = (size_t)c->T * c->d;
-  }
+                       const int32_t* dest_row, const float* topk_w, void* out, hipStream_t s) {
+  const CombineLaunch cl{y_perm, c->n_shared ? y_shared : nullptr, dest_row, topk_w, out, c->T, c->d, c->top_k,
+                         c->out_dtype};
   return launch_combine(cl, s, perm_rows(c));
 }
 
@@ -516,7 +487,7 @@ moe_status moe_expert_ffn(const moe_config* cfg, const void* x, const void* x_pe
   }
   st = check_ws(ws, ws_bytes, layout_of(cfg).ffn_end);
   if (st != MOE_OK) return st;
-  return run_ffn(cfg, x, x_perm, nullptr, offsets, weights, y_perm, y_shared, (char*)ws, true,
+  return run_ffn(cfg, x, x_perm, nullptr, offsets, weights, y_perm, y_shared, (char*)ws,
                  (hipStream_t)stream);
 }
 
@@ -531,7 +502,7 @@ moe_status moe_combine(const moe_config* cfg, const float* y_perm, const float* 
     if (cfg->n_shared && (!y_shared || !aligned16(y_shared)))
       return fail(MOE_ERR_INVALID_ARGUMENT, "y_shared (16-byte aligned) is required with a shared expert");
   }
-  return run_combine(cfg, y_perm, y_shared, dest_row, topk_w, out, nullptr, (hipStream_t)stream);
+  return run_combine(cfg, y_perm, y_shared, dest_row, topk_w, out, (hipStream_t)stream);
 }
 
 moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
@@ -576,10 +547,9 @@ moe_status moe_forward(const moe_config* cfg, const void* x, const float* w_rout
   st = run_permute(cfg, x, idx, counts, offsets, dest, src, ndrop, gather ? nullptr : x_perm, stats, w, s,
                    tiles_in_permute ? (int32_t*)(w + layout_of(cfg).tiles) : nullptr, grouped_gemm_bm(gu));
   if (st != MOE_OK) return st;
-  st = run_ffn(cfg, x, x_perm, gather ? src : nullptr, offsets, weights, y_perm, y_sh, w, false, s,
-               tiles_in_permute);
+  st = run_ffn(cfg, x, x_perm, gather ? src : nullptr, offsets, weights, y_perm, y_sh, w, s, tiles_in_permute);
   if (st != MOE_OK) return st;
-  return run_combine(cfg, y_perm, y_sh, dest, tw, out, w, s);
+  return run_combine(cfg, y_perm, y_sh, dest, tw, out, s);
 }
 
 moe_status moe_forward_noalloc(const moe_config* cfg, const void* x, const float* w_router, const float* bias,
