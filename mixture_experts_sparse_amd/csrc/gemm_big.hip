@@ -25,7 +25,14 @@
 //    twelve fragment reads of a half two per row over the first six rows
 //    (scheduling barriers keep that order), so the memory pipeline never gets
 //    a burst and the reads have landed before the barrier or the next step
-//    waits for them.
+//    waits for them;
+//  * the weights are the MFMA's first operand, so a lane's four results are
+//    consecutive output columns of one token row: the epilogue stores them
+//    straight from the accumulators as 8-byte (h, bf16) or 16-byte (y, f32)
+//    vectors, with no LDS staging and no barrier;
+//  * persistent: one block per CU walks its XCD's share of the units, so a tile
+//    follows the previous one on the same CU with no launch in between
+//    (measured at 8 x 1024 rows, 4096 x 14336: gate/up 1517 -> 1447 us).
 #include <algorithm>
 #include <type_traits>
 
@@ -242,7 +249,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
 #pragma unroll
             for (int e = RPR * i; e < RPR * i + RPR && e < NE; ++e) read_frag(Y, e, sa, sb, a_frag1, b_frag1);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[i], X[8 + j], acc[i][j]);
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(X[8 + j], X[i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
           }
           // step ks + 1 has landed; only the weights of step ks + 2 may still be in flight
@@ -259,7 +266,7 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
 #pragma unroll
             for (int e = RPR * i; e < RPR * i + RPR && e < NE; ++e) read_frag(X, e, na, nb, a_frag0, b_frag0);
 #pragma unroll
-            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[i], Y[8 + j], acc[i][j]);
+            for (int j = 0; j < NJ; ++j) acc[i][j] = mfma16x16x32(Y[8 + j], Y[i], acc[i][j]);
             __builtin_amdgcn_sched_barrier(0);
           }
           __builtin_amdgcn_s_waitcnt(kLgkm0);  // next step's first-half fragments are in
@@ -330,51 +337,37 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
       }
     }
 
-    // ---- epilogue (rows past the group's end are not stored)
-    const int col_in = lane & 15;
-    const int rq = (lane >> 4) * 4;
+    // ---- epilogue, straight from the accumulators (rows past the group's end
+    // are not stored).  With the weights as the MFMA's first operand, lane l
+    // holds token row m = 16 i + l % 16 and the four consecutive output columns
+    // 16 j + 4 (l / 16) + r of it, so every store is one 8- or 16-byte vector.
+    const int mrow = lane & 15;
+    const int nq = (lane >> 4) * 4;
     if (GATED) {
-      // h = silu(g) * u for this wave's 128 rows x WN/2 columns, staged through
-      // LDS (stages are free: every wave has passed its last MFMA once all
-      // waves reach the barrier) and stored as 16-byte row segments.
-      constexpr int HC = WN / 2;                      // h columns per wave
-      constexpr int HROW = HC * 2;                    // bytes per staged row
-      uint8_t* hs = smem + w * (128 * HROW);
-      block_sync();
+      // h = silu(gate) * up: fragment j < NJ / 2 holds gate columns, j + NJ / 2 the matching up columns
+      uint16_t* h = (uint16_t*)p.out + tr.nt * (BNR / 2) + wn * (WN / 2) + nq;
 #pragma unroll
-      for (int j = 0; j < NJ / 2; ++j)
+      for (int i = 0; i < 8; ++i) {
+        const int m = wm * 128 + i * 16 + mrow;
+        if (i >= live || m >= tr.rows) continue;
+        uint16_t* hr = h + (size_t)(tr.row0 + m) * N;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
+        for (int j = 0; j < NJ / 2; ++j) {
+          uint32_t hv[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + rq + r;
-            const uint16_t hv = f32_to_bf16_rne(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
-            *(uint16_t*)(hs + m * HROW + (j * 16 + col_in) * 2) = hv;
-          }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): staged h visible to the wave
-      uint16_t* h = (uint16_t*)p.out;
-      constexpr int SEG = HROW / 16;                  // 16-byte segments per row
-      const int f0 = tr.nt * (BNR / 2) + wn * HC;
-#pragma unroll
-      for (int it = 0; it < 128 * SEG / 64; ++it) {
-        const int idx = it * 64 + lane;
-        const int m = idx / SEG, sg = idx % SEG;
-        const uint4 v = *(const uint4*)(hs + m * HROW + sg * 16);
-        if (wm * 128 + m < tr.rows)
-          *(uint4*)(h + (size_t)(tr.row0 + wm * 128 + m) * N + f0 + sg * 8) = v;
+          for (int r = 0; r < 4; ++r) hv[r] = f32_to_bf16_rne(silu_f32(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+          *(uint2*)(hr + j * 16) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+        }
       }
     } else {
-      float* y = (float*)p.out;
+      float* y = (float*)p.out + tr.nt * BNR + wn * WN + nq;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int n = tr.nt * BNR + wn * WN + j * 16 + col_in;
+      for (int i = 0; i < 8; ++i) {
+        const int m = wm * 128 + i * 16 + mrow;
+        if (i >= live || m >= tr.rows) continue;
+        float* yr = y + (size_t)(tr.row0 + m) * N;
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = wm * 128 + i * 16 + rq + r;
-            if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = acc[i][j][r];
-          }
+        for (int j = 0; j < NJ; ++j) *(f32x4_t*)(yr + j * 16) = acc[i][j];
       }
     }
   }
@@ -395,10 +388,12 @@ moe_status launch_gemm_bf16_big(const GemmLaunch& a, const int32_t* goff, const 
     p.sk_part = a.sk_part;
     p.sk_cnt = a.sk_cnt;
   }
-  // whole tiles plus at most G tail units, spread over the 8 XCDs
-  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles + p.G;
-  int64_t grid = (ceil_div(upper, 8) + 1) * 8;
+  // persistent: one block per CU (rounded down to the 8 XCDs), each taking its
+  // XCD's units in turn, so no block waits for a fresh launch between tiles
+  const int64_t upper = (ceil_div(a.max_rows, kBM) + a.groups) * p.n_tiles;
   if (upper <= 0) return MOE_OK;
+  const int64_t cu8 = std::max<int64_t>(8, device_cu_count() / 8 * 8);
+  const int64_t grid = p.G ? cu8 : std::min<int64_t>(ceil_div(upper, 8) * 8, cu8);
   const char* name = a.shared ? (a.gated ? "shared_gate_up_bf16" : "shared_down_bf16")
                               : (a.gated ? "gemm_gate_up_bf16" : "gemm_down_bf16");
   int tok = begin_launch(name, s);
