@@ -31,6 +31,10 @@ SMALL = {
     # expert take the K-split kernel, more take 64-row tiles or the large tiles)
     "fp8_stream32": W.shrink(WK["skewed_fp8"], T=1500, d=256, F=256),
     "bf16_stream32": WK["mixtral_bf16"].replace(name="bf16s32", T=200, d=512, E=16, k=2, F=256),
+    # fp8 with more rows per expert (capacity 58 and 117): the streaming GEMM's
+    # 64-row tiles, one or two per expert
+    "fp8_stream64": W.shrink(WK["skewed_fp8"], T=3000, d=256, F=256),
+    "fp8_stream128": W.shrink(WK["skewed_fp8"], T=6000, d=256, F=256),
     # decode-sized bf16 batch (8 rows per expert): the K-split GEMM
     "bf16_decode": WK["mixtral_bf16"].replace(name="bf16d", T=64, d=512, E=16, k=2, F=256),
     # overflow re-routing: fp8 skewed (streaming GEMM), bf16 Zipf (large-tile GEMM),
