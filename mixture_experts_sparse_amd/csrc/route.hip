@@ -623,6 +623,50 @@ __global__ __launch_bounds__(256) void topk_kernel(RouteLaunch a) {
   route_token<EPL>(a, t, lane, [&](int e) { return zv[(e - lane) >> 6]; });
 }
 
+// Small batches (at most 256 tokens): one block of four waves per token.  Wave
+// v adds the slices [S v / 4, S (v + 1) / 4) of its lanes' experts -- all of
+// them requested at once, one memory round trip -- and the four sums meet in
+// LDS, added in wave order; wave 0 then runs route_token.  (With one wave per
+// token a 64-slice decode batch makes two round trips: 128 loads per lane are
+// more than the 63 the load counter holds.)
+template <int EPL>
+__global__ __launch_bounds__(256) void topk_quarters_kernel(RouteLaunch a) {
+  constexpr int PQ = 16;  // slices per wave requested together (S <= 64 takes one round)
+  __shared__ float zq[4][EPL][64];
+  const int lane = threadIdx.x & 63;
+  const int v = threadIdx.x >> 6;
+  const int t = blockIdx.x;
+  const int S = a.split, EP = a.ep, T = a.T, E = a.E;
+  const size_t st = (size_t)T * EP;
+  const int s_lo = S * v / 4, s_hi = S * (v + 1) / 4;
+  float zv[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) zv[i] = 0.f;
+  for (int s0 = s_lo; s0 < s_hi; s0 += PQ) {
+    float x[EPL][PQ];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      const int e = lane + 64 * i;
+      const float* pe = a.part + (size_t)t * EP + e;
+#pragma unroll
+      for (int q = 0; q < PQ; ++q) x[i][q] = (s0 + q < s_hi && e < E) ? pe[(size_t)(s0 + q) * st] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < EPL; ++i)
+#pragma unroll
+      for (int q = 0; q < PQ; ++q)
+        if (s0 + q < s_hi) zv[i] += x[i][q];
+  }
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) zq[v][i][lane] = zv[i];
+  __syncthreads();
+  if (v != 0) return;
+  float z[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) z[i] = ((zq[0][i][lane] + zq[1][i][lane]) + zq[2][i][lane]) + zq[3][i][lane];
+  route_token<EPL>(a, t, lane, [&](int e) { return z[(e - lane) >> 6]; });
+}
+
 template <int EP>
 moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   const int kslice = a.d / a.split;
@@ -646,7 +690,7 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
     moe_status st = end_launch(tok, s);
     if (st != MOE_OK) return st;
     tok = begin_launch("route_topk", s);
-    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 32>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((topk_quarters_kernel<(EP + 63) / 64>), dim3((unsigned)a.T), dim3(256), 0, s, a);
     return end_launch(tok, s);
   }
   int tok = begin_launch("router_prep", s);
@@ -661,7 +705,7 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   if (st != MOE_OK) return st;
   tok = begin_launch("route_topk", s);
   if (a.T <= 256)
-    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 32>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((topk_quarters_kernel<(EP + 63) / 64>), dim3((unsigned)a.T), dim3(256), 0, s, a);
   else
     hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 8>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
   return end_launch(tok, s);
