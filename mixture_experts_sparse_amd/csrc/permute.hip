@@ -29,34 +29,59 @@ __device__ __forceinline__ int pair_expert(const int32_t* __restrict__ idx, int 
   return idx[(size_t)(p / k) * ld + (p % k)];
 }
 
+// Inclusive sums of v and v2 over the block's 256 threads (four waves, thread
+// order): shuffles inside each wave, then the wave totals through `tot` (8 ints
+// of LDS).  *ta / *tb get the block totals.  Two barriers in all, where a
+// Hillis-Steele scan over LDS takes sixteen.
+__device__ __forceinline__ void block_scan256(int& v, int& v2, int* tot, int* ta, int* tb) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int a = __shfl_up(v, off), b = __shfl_up(v2, off);
+    if (lane >= off) {
+      v += a;
+      v2 += b;
+    }
+  }
+  if (lane == 63) {
+    tot[w] = v;
+    tot[4 + w] = v2;
+  }
+  __syncthreads();
+  int pa = 0, pb = 0;
+  for (int i = 0; i < w; ++i) {
+    pa += tot[i];
+    pb += tot[4 + i];
+  }
+  *ta = tot[0] + tot[1] + tot[2] + tot[3];
+  *tb = tot[4] + tot[5] + tot[6] + tot[7];
+  v += pa;
+  v2 += pb;
+  __syncthreads();  // tot is free again
+}
+
 // The grouped GEMM's tile lists (the layout tiles_kernel writes: offsets,
 // exclusive prefix of m-tiles per expert, the expert of every m-tile) from the
 // final per-expert row counts, by the one block that knows them.  Thread e holds
 // expert e's kept rows and exclusive row offset; `scan` is 256 ints of LDS.
-__device__ __forceinline__ void write_tile_lists(int e, int kept, int off_excl, int E, int bm, int* scan,
+__device__ __forceinline__ void write_tile_lists(int e, int kept, int off_excl, int E, int bm, int* tot,
                                                  int32_t* __restrict__ tiles, int32_t* __restrict__ sk_zero) {
   if (sk_zero)  // the large-tile GEMM's stream-K counters start at zero
     for (int i = e; i < kSkUnits; i += 256) sk_zero[i] = 0;
   const int nt = (e < E) ? (kept + bm - 1) / bm : 0;
-  scan[e] = nt;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive sum scan
-    const int v = (e >= off) ? scan[e - off] : 0;
-    __syncthreads();
-    scan[e] += v;
-    __syncthreads();
-  }
+  int incl = nt, unused = 0, all_nt, all_unused;
+  block_scan256(incl, unused, tot, &all_nt, &all_unused);
   int32_t* goff = tiles;
   int32_t* tp = tiles + E + 1;
   int32_t* tile_group = tiles + 2 * (E + 1);
   if (e < E) {
     goff[e] = off_excl;
-    tp[e] = scan[e] - nt;
-    for (int m = scan[e] - nt; m < scan[e]; ++m) tile_group[m] = e;
+    tp[e] = incl - nt;
+    for (int m = incl - nt; m < incl; ++m) tile_group[m] = e;
   }
   if (e == E - 1) {
     goff[E] = off_excl + kept;
-    tp[E] = scan[e];
+    tp[E] = incl;
   }
 }
 
@@ -85,45 +110,38 @@ __global__ __launch_bounds__(kThreads) void scan_kernel(int32_t* __restrict__ hi
                                                         int32_t* __restrict__ stats,
                                                         int32_t* __restrict__ tiles, int tile_bm,
                                                         int32_t* __restrict__ sk_zero) {
-  __shared__ int kept_s[256];
-  __shared__ int drop_s[256];
+  __shared__ int tot[8];
   const int e = threadIdx.x;
   int run = 0;
   if (e < E) {
-    for (int b = 0; b < nblk; ++b) {
-      const int c = hist[(size_t)b * E + e];
-      hist[(size_t)b * E + e] = run;
-      run += c;
+    // chunk counts of this expert, sixteen requested at a time, replaced by
+    // the exclusive prefix over chunks
+    for (int b0 = 0; b0 < nblk; b0 += 16) {
+      int c[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) c[u] = b0 + u < nblk ? hist[(size_t)(b0 + u) * E + e] : 0;
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+        if (b0 + u < nblk) {
+          hist[(size_t)(b0 + u) * E + e] = run;
+          run += c[u];
+        }
     }
   }
   const int kept = (e < E) ? (int)((cap >= 0 && (int64_t)run > cap) ? cap : run) : 0;
-  kept_s[e] = kept;
-  drop_s[e] = (e < E) ? run - kept : 0;
-  __syncthreads();
-  // inclusive Hillis-Steele scan of kept over 256 entries
-  for (int off = 1; off < 256; off <<= 1) {
-    int v = (e >= off) ? kept_s[e - off] : 0;
-    int dv = (e >= off) ? drop_s[e - off] : 0;
-    __syncthreads();
-    kept_s[e] += v;
-    drop_s[e] += dv;
-    __syncthreads();
-  }
+  int incl = kept, dincl = (e < E) ? run - kept : 0, all_kept, all_drop;
+  block_scan256(incl, dincl, tot, &all_kept, &all_drop);
   if (e < E) {
     counts[e] = run;
-    offsets[e + 1] = kept_s[e];
+    offsets[e + 1] = incl;
     if (stats) { stats[e] = run; stats[E + e] = kept; }
   }
   if (e == 0) {
     offsets[0] = 0;
-    n_dropped[0] = drop_s[255];
-    if (stats) stats[2 * E] = drop_s[255];
+    n_dropped[0] = all_drop;
+    if (stats) stats[2 * E] = all_drop;
   }
-  if (tiles) {
-    const int incl = kept_s[e];
-    __syncthreads();  // (kept_s is reused as the tile scan)
-    write_tile_lists(e, kept, incl - kept, E, tile_bm, kept_s, tiles, sk_zero);
-  }
+  if (tiles) write_tile_lists(e, kept, incl - kept, E, tile_bm, tot, tiles, sk_zero);
 }
 
 // Stable ranks of the pairs [p0, p1) given running[e] = pairs of expert e before
@@ -212,50 +230,42 @@ __global__ __launch_bounds__(kThreads) void count_rank_kernel(const int32_t* __r
                                                               int32_t* __restrict__ sk_zero) {
   __shared__ int running[256];
   __shared__ int wcnt[4][256];
-  __shared__ int kept_s[256];
-  __shared__ int drop_s[256];
   __shared__ int32_t off_s[257];
+  __shared__ int32_t idx_s[kPermChunk];  // the pairs' experts, read from memory once
+  __shared__ int tot[8];
   const int tid = threadIdx.x;
   running[tid] = 0;
   wcnt[0][tid] = wcnt[1][tid] = wcnt[2][tid] = wcnt[3][tid] = 0;
+  for (int p = tid; p < P; p += kThreads) idx_s[p] = pair_expert(idx, p, k, ld);
   __syncthreads();
   for (int p = tid; p < P; p += kThreads) {
-    const int e = pair_expert(idx, p, k, ld);
+    const int e = idx_s[p];
     if (e >= 0 && e < E) atomicAdd(&running[e], 1);  // ids outside [0,E) are ignored
   }
   __syncthreads();
   const int e = tid;
   const int run = (e < E) ? running[e] : 0;
   const int kept = (e < E) ? (int)((cap >= 0 && (int64_t)run > cap) ? cap : run) : 0;
-  kept_s[e] = kept;
-  drop_s[e] = run - kept;
-  __syncthreads();
-  for (int off = 1; off < 256; off <<= 1) {  // inclusive scans of kept and dropped
-    const int v = (e >= off) ? kept_s[e - off] : 0;
-    const int dv = (e >= off) ? drop_s[e - off] : 0;
-    __syncthreads();
-    kept_s[e] += v;
-    drop_s[e] += dv;
-    __syncthreads();
-  }
+  int incl = kept, dincl = run - kept, all_kept, all_drop;
+  block_scan256(incl, dincl, tot, &all_kept, &all_drop);
   if (e < E) {
     counts[e] = run;
-    offsets[e + 1] = kept_s[e];
-    off_s[e + 1] = kept_s[e];
+    offsets[e + 1] = incl;
+    off_s[e + 1] = incl;
     if (stats) { stats[e] = run; stats[E + e] = kept; }
   }
   if (e == 0) {
     offsets[0] = 0;
     off_s[0] = 0;
-    n_dropped[0] = drop_s[255];
-    if (stats) stats[2 * E] = drop_s[255];
+    n_dropped[0] = all_drop;
+    if (stats) stats[2 * E] = all_drop;
   }
-  __syncthreads();
-  if (tiles) write_tile_lists(e, kept, kept_s[e] - kept, E, tile_bm, drop_s, tiles, sk_zero);
+  if (tiles) write_tile_lists(e, kept, incl - kept, E, tile_bm, tot, tiles, sk_zero);
   running[e] = 0;  // ranks start at zero in the only chunk
   __syncthreads();
   const int n_rows = off_s[E];
-  rank_pairs(idx, 0, P, E, k, ld, cap, off_s, running, wcnt, dest_row, src_token);
+  // the cached experts are laid out [T][k]
+  rank_pairs(idx_s, 0, P, E, k, k, cap, off_s, running, wcnt, dest_row, src_token);
   for (int64_t r = tid; r < rows; r += kThreads)
     if (r >= n_rows) src_token[r] = -1;
 }
