@@ -456,8 +456,8 @@ __global__ __launch_bounds__(512, 1) void router_mfma_kernel(RouterParams p) {
     }
 }
 
-// One token block (T <= 256): the same partial logits as router_prep_kernel +
-// router_mfma_kernel in one launch.  The block splits its own d-slice of W_r
+// The same partial logits as router_prep_kernel + router_mfma_kernel in one
+// launch, block (b, s) taking tokens [256 b, 256 b + 256) over d-slice s.  The block splits its own d-slice of W_r
 // (the same exact hi + mid + lo bf16 split, from f32 rows read coalesced along
 // the experts) into LDS, laid out as router_mfma_kernel's stages one after the
 // other, then runs the same MFMA loop over them in the same order -- so the
@@ -479,8 +479,9 @@ __global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __
   // whose 32 loads all go out before any is used)
   // x fragments: rows wv * 32 + lane % 16 (+ 16), k group lane / 16 of each step
   const int kg = lane >> 4;
-  const uint16_t* xa0 = x + (size_t)min(wv * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
-  const uint16_t* xa1 = x + (size_t)min(wv * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const int t0 = blockIdx.x * 256;
+  const uint16_t* xa0 = x + (size_t)min(t0 + wv * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const uint16_t* xa1 = x + (size_t)min(t0 + wv * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
   constexpr int kPreSteps = 8;
   bf16x8_t xp0[kPreSteps], xp1[kPreSteps];
   if (ksteps <= kPreSteps) {
@@ -583,7 +584,7 @@ __global__ __launch_bounds__(512, 1) void router_fused_kernel(const uint16_t* __
   for (int m = 0; m < 2; ++m)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = wv * 32 + m * 16 + (lane >> 4) * 4 + r;
+      const int t = t0 + wv * 32 + m * 16 + (lane >> 4) * 4 + r;
       if (t < T) {
 #pragma unroll
         for (int n = 0; n < NF; ++n) out[(size_t)t * EP + n * 16 + (lane & 15)] = acc[m][n][r];
@@ -667,11 +668,23 @@ __global__ __launch_bounds__(256) void topk_quarters_kernel(RouteLaunch a) {
   route_token<EPL>(a, t, lane, [&](int e) { return z[(e - lane) >> 6]; });
 }
 
+// the top-k pass over the router's partials: four waves per token for small
+// batches, one otherwise
+template <int EP>
+moe_status launch_topk(const RouteLaunch& a, hipStream_t s) {
+  int tok = begin_launch("route_topk", s);
+  if (a.T <= 256)
+    hipLaunchKernelGGL((topk_quarters_kernel<(EP + 63) / 64>), dim3((unsigned)a.T), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 8>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
+  return end_launch(tok, s);
+}
+
 template <int EP>
 moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   const int kslice = a.d / a.split;
   const size_t fused_lds = (size_t)(kslice / 32) * 3 * EP * 64;
-  if (a.T <= 256 && fused_lds <= kFusedRouterLds && (size_t)kslice * EP <= 16384) {
+  if (fused_lds <= kFusedRouterLds && (size_t)kslice * EP <= 16384) {
     // more than 64 KB of dynamic LDS needs the attribute, set once per device
     // (a repeat after a race between threads is harmless)
     static std::atomic<bool> lds_set[64];
@@ -685,13 +698,11 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
       lds_set[dev].store(true, std::memory_order_release);
     }
     int tok = begin_launch("router_mfma", s);
-    hipLaunchKernelGGL(router_fused_kernel<EP>, dim3(1, a.split), dim3(512), fused_lds, s, (const uint16_t*)a.x,
-                       a.w_router, a.part, a.T, a.d, a.E, kslice);
+    hipLaunchKernelGGL(router_fused_kernel<EP>, dim3((unsigned)ceil_div(a.T, 256), a.split), dim3(512), fused_lds, s,
+                       (const uint16_t*)a.x, a.w_router, a.part, a.T, a.d, a.E, kslice);
     moe_status st = end_launch(tok, s);
     if (st != MOE_OK) return st;
-    tok = begin_launch("route_topk", s);
-    hipLaunchKernelGGL((topk_quarters_kernel<(EP + 63) / 64>), dim3((unsigned)a.T), dim3(256), 0, s, a);
-    return end_launch(tok, s);
+    return launch_topk<EP>(a, s);
   }
   int tok = begin_launch("router_prep", s);
   hipLaunchKernelGGL(router_prep_kernel, dim3(a.d / 64, (unsigned)ceil_div(EP, 64)), dim3(256), 0, s,
@@ -703,12 +714,7 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   hipLaunchKernelGGL(router_mfma_kernel<EP>, dim3((unsigned)ceil_div(a.T, 256), a.split), dim3(512), 0, s, rp);
   st = end_launch(tok, s);
   if (st != MOE_OK) return st;
-  tok = begin_launch("route_topk", s);
-  if (a.T <= 256)
-    hipLaunchKernelGGL((topk_quarters_kernel<(EP + 63) / 64>), dim3((unsigned)a.T), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((topk_kernel<(EP + 63) / 64, 8>), dim3((unsigned)ceil_div(a.T, 4)), dim3(256), 0, s, a);
-  return end_launch(tok, s);
+  return launch_topk<EP>(a, s);
 }
 
 template <bool BF16X, int EMAX, int BT, int ESPLIT, int TM, int TN>
