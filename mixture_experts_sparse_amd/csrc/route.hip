@@ -327,6 +327,9 @@ __global__ __launch_bounds__(256) void route_kernel(RouteLaunch a) {
 // LDS a one-token-block router may hold its whole split d-slice in (dynamic LDS)
 constexpr size_t kFusedRouterLds = 96 * 1024;
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt(n) alone
+constexpr unsigned vmcnt_imm_r(int n) { return 0x0F70u | (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14); }
+
 __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -443,6 +446,122 @@ __global__ __launch_bounds__(512, 1) void router_mfma_kernel(RouterParams p) {
     a0 = n0;
     a1 = n1;
   }
+  float* out = p.part + (size_t)blockIdx.y * T * EP;
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + w * 32 + m * 16 + (lane >> 4) * 4 + r;
+      if (t < T) {
+#pragma unroll
+        for (int n = 0; n < NF; ++n) out[(size_t)t * EP + n * 16 + (lane & 15)] = acc[m][n][r];
+      }
+    }
+}
+
+// router_mfma_kernel with deeper prefetch, for 128 padded experts (every wave
+// then issues the same number of weight loads per step, so the waits can be
+// counted): the x fragments run DX = 3 steps ahead in a register
+// ring, the split weights 2 steps ahead in three LDS stages, and a step waits
+// only for its own loads -- not, as router_mfma_kernel does, for everything in
+// flight.  Same MFMAs in the same order, so the partials are the same bit for
+// bit.
+template <int EP>
+__global__ __launch_bounds__(512, 1) void router_mfma_pipe_kernel(RouterParams p) {
+  constexpr int NF = EP / 16;
+  constexpr int ROWS = 3 * EP;          // B rows: split-major (hi, mid, lo)
+  constexpr int STAGE = ROWS * 64;      // 32 k (64 bytes) per row
+  constexpr int NINS = ROWS / 16;       // 16-row load instructions per stage
+  constexpr int NB = NINS / 8;          // of them per wave
+  constexpr int NS = 3;                 // weight stages (loads 2 steps ahead)
+  constexpr int DX = 3;                 // x fragment ring (loads 3 steps ahead)
+  static_assert(NINS % 8 == 0, "every wave issues the same weight loads");
+  // loads issued after the later of a step's own (its weights, issued two steps
+  // before it, after its x fragments): the next step's x (2), then one step's
+  // weights and x (NB + 2)
+  constexpr int kWait = 2 + NB + 2;
+  static_assert(kWait <= 63, "vmcnt holds at most 63 loads");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = p.T, d = p.d;
+  const int t0 = blockIdx.x * 256;
+  const int kb = blockIdx.y * p.kslice, ksteps = p.kslice / 32;
+  const int kg = lane >> 4;
+  const uint16_t* xa0 = p.x + (size_t)min(t0 + w * 32 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const uint16_t* xa1 = p.x + (size_t)min(t0 + w * 32 + 16 + (lane & 15), T - 1) * d + kb + kg * 8;
+  const int dr = lane >> 2;
+  const int dc = (lane & 3) ^ ((dr >> 1) & 3);
+  const uint16_t* wsrc = p.wt + (size_t)dr * d + kb + dc * 8;
+  const uint32_t bfrag = (uint32_t)((lane & 15) * 64 + ((kg ^ (((lane & 15) >> 1) & 3)) * 16));
+  // loads of step ks (clamped to the last step: a refill past the end lands in a
+  // stage or ring slot no later step reads)
+  auto issue_b = [&](int ks) {
+    const int kc = min(ks, ksteps - 1);
+    uint8_t* st = smem + (ks % NS) * STAGE;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int q = w + 8 * i;
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(wsrc + (size_t)q * 16 * d + kc * 32), MOE_LPTR(st + q * 1024), 16,
+                                       0, 0);
+    }
+  };
+  bf16x8_t xr0[DX], xr1[DX];
+  auto issue_x = [&](int slot, int ks) {
+    const int kc = min(ks, ksteps - 1);
+    xr0[slot] = *(const bf16x8_t*)(xa0 + kc * 32);
+    xr1[slot] = *(const bf16x8_t*)(xa1 + kc * 32);
+  };
+  f32x4_t acc[2][NF];
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < NF; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // issue order: B(0) x(0) B(1) x(1) x(2), then step j issues B(j + 2) x(j + 3);
+  // so after the later of B(j), x(j) come x(j + 1), B(j + 1), x(j + 2) -- kWait loads
+  issue_b(0);
+  asm volatile("" ::: "memory");
+  issue_x(0, 0);
+  asm volatile("" ::: "memory");
+  issue_b(1);
+  asm volatile("" ::: "memory");
+  issue_x(1, 1);
+  asm volatile("" ::: "memory");
+  issue_x(2, 2);
+  asm volatile("" ::: "memory");
+  auto step = [&](int ks, int slot) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm_r(kWait));  // B(ks) and x(ks) have landed
+    __builtin_amdgcn_s_waitcnt(0xC07F);            // this wave's reads of step ks - 1 are done
+    bar();                                         // every wave's are: stage (ks + 2) % 3 is free
+    __builtin_amdgcn_sched_barrier(0);
+    const bf16x8_t a0 = xr0[slot], a1 = xr1[slot];
+    issue_b(ks + 2);
+    asm volatile("" ::: "memory");
+    issue_x(slot, ks + 3);  // the ring slot this step has just taken its fragments from
+    asm volatile("" ::: "memory");
+    const uint8_t* st = smem + (ks % NS) * STAGE;
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+      const bf16x8_t bh = *(const bf16x8_t*)(st + bfrag + (n * 16) * 64);
+      const bf16x8_t bm = *(const bf16x8_t*)(st + bfrag + (EP + n * 16) * 64);
+      const bf16x8_t bl = *(const bf16x8_t*)(st + bfrag + (2 * EP + n * 16) * 64);
+      acc[0][n] = mfma16x16x32(a0, bh, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bh, acc[1][n]);
+      acc[0][n] = mfma16x16x32(a0, bm, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bm, acc[1][n]);
+      acc[0][n] = mfma16x16x32(a0, bl, acc[0][n]);
+      acc[1][n] = mfma16x16x32(a1, bl, acc[1][n]);
+    }
+  };
+  int ks = 0;
+  for (; ks + DX <= ksteps; ks += DX) {
+#pragma unroll
+    for (int u = 0; u < DX; ++u) step(ks + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < DX - 1; ++u)
+    if (ks + u < ksteps) step(ks + u, u);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm_r(0));  // no load may land in LDS after the block ends
   float* out = p.part + (size_t)blockIdx.y * T * EP;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -711,7 +830,13 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
   if (st != MOE_OK) return st;
   RouterParams rp{(const uint16_t*)a.x, a.wt, a.part, a.T, a.d, a.d / a.split};
   tok = begin_launch("router_mfma", s);
-  hipLaunchKernelGGL(router_mfma_kernel<EP>, dim3((unsigned)ceil_div(a.T, 256), a.split), dim3(512), 0, s, rp);
+  // 128 padded experts: the pipelined loop (skewed fp8 layer 57.1 -> 52.4 us); at
+  // 256 its 256 VGPRs spill and it ran slower (89 -> 105 us), so that width keeps
+  // the plain loop
+  if constexpr (EP == 128)
+    hipLaunchKernelGGL(router_mfma_pipe_kernel<EP>, dim3((unsigned)ceil_div(a.T, 256), a.split), dim3(512), 0, s, rp);
+  else
+    hipLaunchKernelGGL(router_mfma_kernel<EP>, dim3((unsigned)ceil_div(a.T, 256), a.split), dim3(512), 0, s, rp);
   st = end_launch(tok, s);
   if (st != MOE_OK) return st;
   return launch_topk<EP>(a, s);
