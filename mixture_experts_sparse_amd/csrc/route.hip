@@ -336,43 +336,51 @@ __device__ __forceinline__ void bar() {
   asm volatile("" ::: "memory");
 }
 
-// W_r [d][E] f32 -> Wt [3][EP][d] bf16 (rows e >= E are zero).  Block: 64 k x 64 e.
+// W_r [d][E] f32 -> Wt [3][EP][d] bf16 (rows e >= E are zero).  Block: 32 k x
+// 64 e, one 8-wide k chunk of one expert per thread; the tile's eight loads per
+// thread are all requested before any is used.
 __global__ __launch_bounds__(256) void router_prep_kernel(const float* __restrict__ w, uint16_t* __restrict__ wt,
                                                           int d, int E, int EP) {
-  __shared__ float tile[64][65];
-  const int k0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  for (int i = threadIdx.x; i < 64 * 64; i += 256) {
+  __shared__ float tile[32][65];
+  const int k0 = blockIdx.x * 32, e0 = blockIdx.y * 64;
+  float v8[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = threadIdx.x + u * 256;
     const int r = i / 64, c = i % 64;
-    tile[r][c] = (e0 + c < E) ? w[(size_t)(k0 + r) * E + e0 + c] : 0.f;
+    v8[u] = (e0 + c < E) ? w[(size_t)(k0 + r) * E + e0 + c] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = threadIdx.x + u * 256;
+    tile[i / 64][i % 64] = v8[u];
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < 64 * 8; i += 256) {
-    const int el = i / 8, kc = i % 8;  // expert, 8-wide k chunk
-    const int e = e0 + el;
-    if (e >= EP) continue;
-    uint32_t hi[4], mid[4], lo[4];
+  const int el = threadIdx.x / 4, kc = threadIdx.x % 4;  // expert, 8-wide k chunk
+  const int e = e0 + el;
+  if (e >= EP) return;
+  uint32_t hi[4], mid[4], lo[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      uint32_t h2 = 0, m2 = 0, l2 = 0;
+  for (int q = 0; q < 4; ++q) {
+    uint32_t h2 = 0, m2 = 0, l2 = 0;
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float v = tile[kc * 8 + q * 2 + h][el];
-        const uint16_t bh = f32_to_bf16_rne(v);
-        const float r1 = v - bf16_bits_to_f32(bh);
-        const uint16_t bm = f32_to_bf16_rne(r1);
-        const float r2 = r1 - bf16_bits_to_f32(bm);
-        const uint16_t bl = f32_to_bf16_rne(r2);
-        h2 |= (uint32_t)bh << (16 * h);
-        m2 |= (uint32_t)bm << (16 * h);
-        l2 |= (uint32_t)bl << (16 * h);
-      }
-      hi[q] = h2; mid[q] = m2; lo[q] = l2;
+    for (int h = 0; h < 2; ++h) {
+      const float v = tile[kc * 8 + q * 2 + h][el];
+      const uint16_t bh = f32_to_bf16_rne(v);
+      const float r1 = v - bf16_bits_to_f32(bh);
+      const uint16_t bm = f32_to_bf16_rne(r1);
+      const float r2 = r1 - bf16_bits_to_f32(bm);
+      const uint16_t bl = f32_to_bf16_rne(r2);
+      h2 |= (uint32_t)bh << (16 * h);
+      m2 |= (uint32_t)bm << (16 * h);
+      l2 |= (uint32_t)bl << (16 * h);
     }
-    const size_t o = (size_t)e * d + k0 + kc * 8;
-    *(uint4*)(wt + o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-    *(uint4*)(wt + (size_t)EP * d + o) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
-    *(uint4*)(wt + (size_t)2 * EP * d + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    hi[q] = h2; mid[q] = m2; lo[q] = l2;
   }
+  const size_t o = (size_t)e * d + k0 + kc * 8;
+  *(uint4*)(wt + o) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  *(uint4*)(wt + (size_t)EP * d + o) = make_uint4(mid[0], mid[1], mid[2], mid[3]);
+  *(uint4*)(wt + (size_t)2 * EP * d + o) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
 }
 
 struct RouterParams {
@@ -824,7 +832,7 @@ moe_status launch_mfma_route(const RouteLaunch& a, hipStream_t s) {
     return launch_topk<EP>(a, s);
   }
   int tok = begin_launch("router_prep", s);
-  hipLaunchKernelGGL(router_prep_kernel, dim3(a.d / 64, (unsigned)ceil_div(EP, 64)), dim3(256), 0, s,
+  hipLaunchKernelGGL(router_prep_kernel, dim3(a.d / 32, (unsigned)ceil_div(EP, 64)), dim3(256), 0, s,
                      a.w_router, a.wt, a.d, a.E, EP);
   moe_status st = end_launch(tok, s);
   if (st != MOE_OK) return st;
