@@ -135,16 +135,8 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
   constexpr int NF = 4;                    // n-fragments (16 weight rows) per wave
   constexpr int AROW = kKS * 2;            // 256 bytes per activation row
   constexpr int ASTAGE = BM * AROW;
-  constexpr int A_INS = BM / 16;           // 1 KB (4 rows) DMA instructions per wave per step
   constexpr int PD = PL::PD, DA = PL::DA, R = PD + 1, NST = DA + 1;
   constexpr int NB = NF * (PL::RAW + PL::NQ);  // weight loads per wave per step
-  // loads issued after the last one step k needs (weights of k from step k - PD,
-  // activations of k from step k - DA, each step issuing weights then activations)
-  constexpr int kWaitBody = (DA > PD ? A_INS : 0) + (PD - 1) * (A_INS + NB);
-  // past the main loop the weight prefetches feed no step, the compiler drops
-  // them, and only the activation loads remain behind
-  constexpr int kWaitTail = (DA > PD ? A_INS : 0) + (PD - 1) * A_INS;
-  static_assert(kWaitBody <= 63, "vmcnt holds at most 63 loads");
   __shared__ __attribute__((aligned(1024))) uint8_t As[NST * ASTAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -160,8 +152,9 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
   const f32x4_t zero4 = {0.f, 0.f, 0.f, 0.f};
   const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u));
 
-  // activation DMA: instruction i of wave w covers rows 4 (w A_INS + i) .. + 3;
-  // lane: row (lane >> 4), slot (lane & 15) <- chunk slot ^ (row & 15)
+  // activation DMA: instruction i of wave w covers rows 16 i + 4 w .. + 3 (so the
+  // first i instructions of every wave fill the first i 16-row groups); lane: row
+  // (lane >> 4), slot (lane & 15) <- chunk slot ^ (row & 15)
   const int dma_r = lane >> 4;
   // fragment read for sub-step s, m-fragment i: row 16 i + r16, chunk kchunk(g4, s)
   const uint32_t afrag = (uint32_t)(r16 * AROW);
@@ -172,10 +165,10 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
     // rows past the group's end repeat its last row; with a gather map the rows
     // come straight from the token matrix (offsets checked to fit 32 bits)
     const uint8_t* a_base = (const uint8_t*)p.A + (p.gather ? 0 : (size_t)tr.row0 * K * 2);
-    uint32_t a_off[A_INS];
+    uint32_t a_off[MF];
 #pragma unroll
-    for (int i = 0; i < A_INS; ++i) {
-      const int r = (w * A_INS + i) * 4 + dma_r;
+    for (int i = 0; i < MF; ++i) {
+      const int r = 16 * i + 4 * w + dma_r;
       const int c = (lane & 15) ^ (r & 15);
       const int rr = min(r, tr.rows - 1);
       const uint32_t src = p.gather ? (uint32_t)p.gather[tr.row0 + rr] : (uint32_t)rr;
@@ -202,12 +195,14 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       b_row[j] = (const uint8_t*)base + row * RB + (size_t)g4 * 16;
       q_row[j] = (const uint32_t*)qbase + row * KG;
     }
-    auto issue_a = [&](int ks) {
+    // the activation loads of step ks: the NL live 16-row groups only
+    auto issue_a = [&](int ks, auto nl) {
+      constexpr int NL = decltype(nl)::value;
       uint8_t* st = As + (ks % NST) * ASTAGE;
       const uint32_t kb = (uint32_t)min(ks, ksteps - 1) * AROW;
 #pragma unroll
-      for (int i = 0; i < A_INS; ++i)
-        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[i] + kb), MOE_LPTR(st + (w * A_INS + i) * 1024),
+      for (int i = 0; i < NL; ++i)
+        __builtin_amdgcn_global_load_lds(MOE_GPTR(a_base + a_off[i] + kb), MOE_LPTR(st + (4 * i + w) * 1024),
                                          16, 0, 0);
     };
     auto load_w = [&](WSet<WT, NF>& d, int ks) {
@@ -223,119 +218,136 @@ __global__ __launch_bounds__(256, 2) void gemm_stream_kernel(StreamParams p) {
       }
     };
 
-    f32x4_t acc[MF][NF];
+    // the tile, for NL live 16-row groups (rows past the group's end fill the last
+    // group; whole groups past it are neither loaded nor multiplied)
+    auto run_tile = [&](auto nl) {
+      constexpr int NL = decltype(nl)::value;
+      // loads issued after the last one step k needs (weights of k from step k - PD,
+      // activations of k from step k - DA, each step issuing weights then activations)
+      constexpr int kWaitBody = (DA > PD ? NL : 0) + (PD - 1) * (NL + NB);
+      // past the main loop the weight prefetches feed no step, the compiler drops
+      // them, and only the activation loads remain behind
+      constexpr int kWaitTail = (DA > PD ? NL : 0) + (PD - 1) * NL;
+      static_assert(kWaitBody <= 63, "vmcnt holds at most 63 loads");
+      f32x4_t acc[NL][NF];
 #pragma unroll
-    for (int i = 0; i < MF; ++i)
+      for (int i = 0; i < NL; ++i)
 #pragma unroll
-      for (int j = 0; j < NF; ++j) acc[i][j] = zero4;
-    WSet<WT, NF> ring[R];
+        for (int j = 0; j < NF; ++j) acc[i][j] = zero4;
+      WSet<WT, NF> ring[R];
 
-    // one K step: weights of `ks` in cur; weights of ks + PD requested into nxt
-    auto step = [&](int ks, const WSet<WT, NF>& cur, WSet<WT, NF>& nxt, auto tail) {
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(tail)::value ? kWaitTail : kWaitBody));
-      // this wave's LDS reads of step ks - 1 are complete before the barrier:
-      // after it, another wave may refill that stage
-      __builtin_amdgcn_s_waitcnt(kLgkm0);
-      block_sync();
-      __builtin_amdgcn_sched_barrier(0);  // nothing of this step moves above the waits
-      load_w(nxt, ks + PD);
-      issue_fence();
-      issue_a(ks + DA);
-      issue_fence();
-      const uint8_t* st = As + (ks % NST) * ASTAGE;
-      f32x4_t t[MF][NF], rs[MF];
+      // one K step: weights of `ks` in cur; weights of ks + PD requested into nxt
+      auto step = [&](int ks, const WSet<WT, NF>& cur, WSet<WT, NF>& nxt, auto tail) {
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(decltype(tail)::value ? kWaitTail : kWaitBody));
+        // this wave's LDS reads of step ks - 1 are complete before the barrier:
+        // after it, another wave may refill that stage
+        __builtin_amdgcn_s_waitcnt(kLgkm0);
+        block_sync();
+        __builtin_amdgcn_sched_barrier(0);  // nothing of this step moves above the waits
+        load_w(nxt, ks + PD);
+        issue_fence();
+        issue_a(ks + DA, nl);
+        issue_fence();
+        const uint8_t* st = As + (ks % NST) * ASTAGE;
+        f32x4_t t[NL][NF], rs[NL];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t slot = (uint32_t)((kchunk<WT>(g4, s) ^ r16) * 16);
-        bf16x8_t af[MF], bf[NF];
+        for (int s = 0; s < 4; ++s) {
+          const uint32_t slot = (uint32_t)((kchunk<WT>(g4, s) ^ r16) * 16);
+          bf16x8_t af[NL], bf[NF];
 #pragma unroll
-        for (int i = 0; i < MF; ++i) af[i] = *(const bf16x8_t*)(st + afrag + i * 16 * AROW + slot);
+          for (int i = 0; i < NL; ++i) af[i] = *(const bf16x8_t*)(st + afrag + i * 16 * AROW + slot);
 #pragma unroll
-        for (int j = 0; j < NF; ++j) bf[j] = b_frag<WT>(cur.w[j], s);
+          for (int j = 0; j < NF; ++j) bf[j] = b_frag<WT>(cur.w[j], s);
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          if constexpr (WT == WT_INT4) {
-            rs[i] = mfma16x16x32(af[i], ones, s == 0 ? zero4 : rs[i]);
+          for (int i = 0; i < NL; ++i) {
+            if constexpr (WT == WT_INT4) {
+              rs[i] = mfma16x16x32(af[i], ones, s == 0 ? zero4 : rs[i]);
 #pragma unroll
-            for (int j = 0; j < NF; ++j) t[i][j] = mfma16x16x32(af[i], bf[j], s == 0 ? zero4 : t[i][j]);
-          } else {
+              for (int j = 0; j < NF; ++j) t[i][j] = mfma16x16x32(af[i], bf[j], s == 0 ? zero4 : t[i][j]);
+            } else {
 #pragma unroll
-            for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+              for (int j = 0; j < NF; ++j) acc[i][j] = mfma16x16x32(af[i], bf[j], acc[i][j]);
+            }
           }
         }
+        if constexpr (WT == WT_INT4) {
+#pragma unroll
+          for (int j = 0; j < NF; ++j) {
+            const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.q[j][0] & 0xFFFFu));
+            const float c = (float)(128u + ((cur.q[j][0] >> 16) & 15u));
+#pragma unroll
+            for (int i = 0; i < NL; ++i)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, fmaf(-c, rs[i][r], t[i][j][r]), acc[i][j][r]);
+          }
+        }
+      };
+
+      block_sync();  // the previous tile's stages are free
+      // issue order: step j (j = -DA .. -1 here, then 0, 1, ...) issues the weights
+      // of j + PD and then the activations of j + DA
+#pragma unroll
+      for (int j = -DA; j < 0; ++j) {
+        if (j + PD >= 0) load_w(ring[j + PD], j + PD);
+        issue_fence();
+        issue_a(j + DA, nl);
+        issue_fence();
       }
-      if constexpr (WT == WT_INT4) {
+      // step k computes from set k % R and refills set (k + PD) % R, the one step
+      // k - 1 used; whole rounds of R steps, then the remaining steps
+      int ks = 0;
+      for (; ks + R <= ksteps; ks += R) {
+#pragma unroll
+        for (int u = 0; u < R; ++u) step(ks + u, ring[u], ring[(u + PD) % R], std::false_type{});
+      }
+#pragma unroll
+      for (int u = 0; u < R - 1; ++u)
+        if (ks + u < ksteps) step(ks + u, ring[u], ring[(u + PD) % R], std::true_type{});
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
+
+      // ---- epilogue (rows past the group's end are not stored)
+      const int rq = g4 * 4;
+      if (GATED) {
+        uint16_t* h = (uint16_t*)p.out;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int f = tr.nt * 128 + w * 32 + j * 16 + r16;
+          float sg = 1.f, su = 1.f;
+          if constexpr (WT == WT_FP8) {
+            sg = ((const float*)p.S0)[(size_t)g * N + f];
+            su = ((const float*)p.S1)[(size_t)g * N + f];
+          }
+#pragma unroll
+          for (int i = 0; i < NL; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int m = i * 16 + rq + r;
+              if (m < tr.rows)
+                h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(acc[i][j][r] * sg) * (acc[i][j + 2][r] * su));
+            }
+        }
+      } else {
+        float* y = (float*)p.out;
 #pragma unroll
         for (int j = 0; j < NF; ++j) {
-          const float sc = (float)__builtin_bit_cast(_Float16, (uint16_t)(cur.q[j][0] & 0xFFFFu));
-          const float c = (float)(128u + ((cur.q[j][0] >> 16) & 15u));
+          const int n = tr.nt * 256 + w * 64 + j * 16 + r16;
+          float sd = 1.f;
+          if constexpr (WT == WT_FP8) sd = ((const float*)p.S0)[(size_t)g * N + n];
 #pragma unroll
-          for (int i = 0; i < MF; ++i)
+          for (int i = 0; i < NL; ++i)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[i][j][r] = fmaf(sc, fmaf(-c, rs[i][r], t[i][j][r]), acc[i][j][r]);
+            for (int r = 0; r < 4; ++r) {
+              const int m = i * 16 + rq + r;
+              if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = acc[i][j][r] * sd;
+            }
         }
       }
     };
-
-    block_sync();  // the previous tile's stages are free
-    // issue order: step j (j = -DA .. -1 here, then 0, 1, ...) issues the weights
-    // of j + PD and then the activations of j + DA
-#pragma unroll
-    for (int j = -DA; j < 0; ++j) {
-      if (j + PD >= 0) load_w(ring[j + PD], j + PD);
-      issue_fence();
-      issue_a(j + DA);
-      issue_fence();
-    }
-    // step k computes from set k % R and refills set (k + PD) % R, the one step
-    // k - 1 used; whole rounds of R steps, then the remaining steps
-    int ks = 0;
-    for (; ks + R <= ksteps; ks += R) {
-#pragma unroll
-      for (int u = 0; u < R; ++u) step(ks + u, ring[u], ring[(u + PD) % R], std::false_type{});
-    }
-#pragma unroll
-    for (int u = 0; u < R - 1; ++u)
-      if (ks + u < ksteps) step(ks + u, ring[u], ring[(u + PD) % R], std::true_type{});
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this tile
-
-    // ---- epilogue (rows past the group's end are not stored)
-    const int rq = g4 * 4;
-    if (GATED) {
-      uint16_t* h = (uint16_t*)p.out;
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int f = tr.nt * 128 + w * 32 + j * 16 + r16;
-        float sg = 1.f, su = 1.f;
-        if constexpr (WT == WT_FP8) {
-          sg = ((const float*)p.S0)[(size_t)g * N + f];
-          su = ((const float*)p.S1)[(size_t)g * N + f];
-        }
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + rq + r;
-            if (m < tr.rows)
-              h[(size_t)(tr.row0 + m) * N + f] = f32_to_bf16_rne(silu_f32(acc[i][j][r] * sg) * (acc[i][j + 2][r] * su));
-          }
-      }
-    } else {
-      float* y = (float*)p.out;
-#pragma unroll
-      for (int j = 0; j < NF; ++j) {
-        const int n = tr.nt * 256 + w * 64 + j * 16 + r16;
-        float sd = 1.f;
-        if constexpr (WT == WT_FP8) sd = ((const float*)p.S0)[(size_t)g * N + n];
-#pragma unroll
-        for (int i = 0; i < MF; ++i)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = i * 16 + rq + r;
-            if (m < tr.rows) y[(size_t)(tr.row0 + m) * N + n] = acc[i][j][r] * sd;
-          }
-      }
-    }
+    const int nl = min(MF, (tr.rows + 15) >> 4);
+    if (nl >= MF) run_tile(std::integral_constant<int, MF>{});
+    else if (MF == 4 && nl == 3) run_tile(std::integral_constant<int, (MF > 3 ? 3 : 1)>{});
+    else if (nl == 2) run_tile(std::integral_constant<int, (MF > 2 ? 2 : 1)>{});
+    else run_tile(std::integral_constant<int, 1>{});
   }
 }
 
