@@ -206,9 +206,9 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(8 + B_INS));  // step 0 has landed
     block_sync();
 
-    // 16-row groups of this wave's 128 rows that hold rows of the tile, rounded
-    // up to even: the MFMA rows of the others would only multiply padding
-    const int live = min(8, max(0, tr.rows - wm * 128 + 31) / 32 * 2);
+    // 16-row groups of this wave's 128 rows that hold rows of the tile: the MFMA
+    // rows of the others would only multiply padding
+    const int live = min(8, max(0, tr.rows - wm * 128 + 15) / 16);
     // fragment entry e of a half: weights first (every MFMA row needs all of
     // them), then the activation rows
     auto read_frag = [&](bf16x8_t (&F)[8 + NJ], int e, const uint8_t* sa, const uint8_t* sb, uint32_t af,
@@ -276,9 +276,13 @@ __global__ __launch_bounds__(512, 1) void gemm_bf16_big_kernel(BigParams p) {
     };
     switch (live) {
       case 8: k_loop(std::integral_constant<int, 8>{}); break;
+      case 7: k_loop(std::integral_constant<int, 7>{}); break;
       case 6: k_loop(std::integral_constant<int, 6>{}); break;
+      case 5: k_loop(std::integral_constant<int, 5>{}); break;
       case 4: k_loop(std::integral_constant<int, 4>{}); break;
+      case 3: k_loop(std::integral_constant<int, 3>{}); break;
       case 2: k_loop(std::integral_constant<int, 2>{}); break;
+      case 1: k_loop(std::integral_constant<int, 1>{}); break;
       default: k_loop(std::integral_constant<int, 0>{}); break;
     }
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // no load may land in a stage after this unit

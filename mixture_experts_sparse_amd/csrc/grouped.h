@@ -29,10 +29,13 @@ __device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int 
   return r;
 }
 
-// The same walk with the group's rows spread evenly over its m-tiles: a group
-// of c rows in mt = ceil(c / bm) tiles gives tile mi the rows
-// [c mi / mt, c (mi + 1) / mt), so tile heights differ by at most one and no
-// tile is a sliver of a few rows (a sliver costs nearly a whole tile's loads).
+// The same walk with the group's rows spread evenly over its m-tiles in whole
+// 16-row MFMA groups: a group of c rows holds G = ceil(c / 16) such groups, and
+// of its mt = ceil(c / bm) tiles, tile mi takes groups [G mi / mt, G (mi + 1) / mt)
+// (rows past c cut off).  Tile heights then differ by at most 16 rows, no tile
+// is a sliver of a few rows (a sliver costs nearly a whole tile's loads), and
+// only the group's last 16-row group can hold padding rows.  G >= mt, so no
+// tile is empty, and G <= 16 mt keeps every tile within bm = 256 rows.
 __device__ __forceinline__ TileRef map_tile_balanced(int L, int n_tiles, int groups,
                                                      const int32_t* __restrict__ tp,
                                                      const int32_t* __restrict__ goff) {
@@ -41,7 +44,8 @@ __device__ __forceinline__ TileRef map_tile_balanced(int L, int n_tiles, int gro
   const int local = L - tp[g] * n_tiles;
   const int nt = local / mt, mi = local % mt;
   const int c = goff[g + 1] - goff[g];
-  const int a = (int)(((int64_t)c * mi) / mt), b = (int)(((int64_t)c * (mi + 1)) / mt);
+  const int G = (c + 15) >> 4;
+  const int a = (int)(((int64_t)G * mi) / mt) * 16, b = min(c, (int)(((int64_t)G * (mi + 1)) / mt) * 16);
   TileRef r;
   r.g = g;
   r.nt = nt;
