@@ -36,22 +36,40 @@ __device__ __forceinline__ TileRef map_tile(int L, int n_tiles, int groups, int 
 // is a sliver of a few rows (a sliver costs nearly a whole tile's loads), and
 // only the group's last 16-row group can hold padding rows.  G >= mt, so no
 // tile is empty, and G <= 16 mt keeps every tile within bm = 256 rows.
+//
+// Order: a group of more than kBand m-tiles is cut into nb = ceil(mt / kBand)
+// bands of about equal height (band b = m-tiles [mt b / nb, mt (b + 1) / nb)),
+// walked one after the other, each n-tile by n-tile with its m-tiles
+// consecutive.  Tiles that run at the same time on an XCD then share about
+// kBand activation tiles and a few weight tiles -- instead of one weight tile
+// and one activation tile per tile when a group has dozens of m-tiles -- and
+// the loads that miss L2 drop accordingly.  With mt <= kBand (one band) the
+// walk is the plain n-tile-major one.
+constexpr int kBand = 8;
+
 __device__ __forceinline__ TileRef map_tile_balanced(int L, int n_tiles, int groups,
                                                      const int32_t* __restrict__ tp,
                                                      const int32_t* __restrict__ goff) {
   const int g = tp[groups + 1 + L / n_tiles];
   const int mt = tp[g + 1] - tp[g];
   const int local = L - tp[g] * n_tiles;
-  const int nt = local / mt, mi = local % mt;
+  // the band holding m-tile row local / n_tiles (bands start at m-tile mt b / nb)
+  const int nb = (mt + kBand - 1) / kBand;
+  const int r = local / n_tiles;
+  int b = r * nb / mt;
+  if (mt * (b + 1) / nb <= r) ++b;
+  const int m0 = mt * b / nb, h = mt * (b + 1) / nb - m0;
+  const int rem = local - m0 * n_tiles;
+  const int nt = rem / h, mi = m0 + rem % h;
   const int c = goff[g + 1] - goff[g];
   const int G = (c + 15) >> 4;
-  const int a = (int)(((int64_t)G * mi) / mt) * 16, b = min(c, (int)(((int64_t)G * (mi + 1)) / mt) * 16);
-  TileRef r;
-  r.g = g;
-  r.nt = nt;
-  r.row0 = goff[g] + a;
-  r.rows = b - a;
-  return r;
+  const int a = (int)(((int64_t)G * mi) / mt) * 16, e = min(c, (int)(((int64_t)G * (mi + 1)) / mt) * 16);
+  TileRef t;
+  t.g = g;
+  t.nt = nt;
+  t.row0 = goff[g] + a;
+  t.rows = e - a;
+  return t;
 }
 
 // bf16 large-tile grouped GEMM (gemm_big.hip): block tile 256 x 256, 8 waves of 128 x 64

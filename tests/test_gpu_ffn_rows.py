@@ -1,8 +1,9 @@
 """The expert FFN (moe_expert_ffn) at chosen rows per expert, against the
 oracle's expert outputs: counts that put every number of live 16-row groups
 into the streaming GEMM's 64- and 32-row tiles (bf16, fp8 and INT4 weights),
-and every number of live 32-row groups into both 128-row halves of the
-large-tile GEMM's 256-row tiles, next to empty experts.
+and every number of live 16-row groups into both 128-row halves of the
+large-tile GEMM's 256-row tiles, next to empty experts; and experts of more
+than eight large tiles, whose tiles the large-tile GEMM walks in bands.
 
 y[r] = (silu(x[r] W_gate[e]^T) * (x[r] W_up[e]^T)) W_down[e]^T for the rows r
 of expert e (page "GPT-4 has 1.8T parameters but uses 2% per token" (mlqm.cn),
@@ -27,6 +28,9 @@ pytestmark = pytest.mark.gpu
 COUNTS_A = [1, 15, 16, 17, 31, 32, 33, 47, 48, 49, 63, 64, 65, 97, 0, 130]
 COUNTS_B = [1, 15, 16, 17, 31, 32, 33, 0, 5, 20, 40, 50, 63, 64, 65, 2]
 COUNTS_C = [1, 31, 32, 33, 127, 128, 129, 255, 256, 257, 300, 0, 513, 64, 96, 160]
+# 8 experts, 9867 rows -> 1234 per expert: large tiles; experts of 10, 17 and 9
+# m-tiles are walked in 2, 3 and 2 bands (at most 8 m-tiles per band)
+COUNTS_D = [2500, 1, 4200, 300, 0, 17, 2049, 800]
 
 CASES = {
     "bf16_tiles64": (W.DT_BF16, COUNTS_A),
@@ -34,6 +38,7 @@ CASES = {
     "fp8_tiles32": (W.DT_FP8, COUNTS_B),
     "int4_tiles32": (W.DT_INT4, COUNTS_B),
     "bf16_big": (W.DT_BF16, COUNTS_C),
+    "bf16_big_bands": (W.DT_BF16, COUNTS_D),
 }
 
 
@@ -43,7 +48,8 @@ def test_expert_ffn_every_live_row_group(name):
     dev = torch.device("cuda")
     w_dtype, counts = CASES[name]
     R = int(sum(counts))
-    sh = W.WORKLOADS["mixtral_bf16"].replace(name=f"rows_{name}", T=R, d=256, E=len(counts), k=1, F=256,
+    F = 512 if name == "bf16_big_bands" else 256  # (four gate/up n-tiles per band row)
+    sh = W.WORKLOADS["mixtral_bf16"].replace(name=f"rows_{name}", T=R, d=256, E=len(counts), k=1, F=F,
                                              w_dtype=w_dtype)
     G.banner(f"ffn rows {name} R={R} w={w_dtype}")
     inp = W.make_inputs(sh, device=dev)
