@@ -8,7 +8,8 @@
 // built around streaming them once at full bandwidth:
 //
 //  * block = 4 waves x 64 weight rows (256 per block), tile = BM = 16 MF rows
-//    of the expert (MF = 2 or 4) -- small tiles waste little MFMA work;
+//    of the expert (MF = 2 or 4), of which only the live 16-row groups (those
+//    holding rows of the expert) are loaded and multiplied;
 //  * each wave loads its own weight rows straight into registers, 128 k per
 //    step (one 128-byte line per fp8 row, two per bf16 row, half a line per
 //    INT4 row), into a ring of register sets PD steps ahead;
