@@ -32,7 +32,12 @@
 //    vectors, with no LDS staging and no barrier;
 //  * persistent: one block per CU walks its XCD's share of the units, so a tile
 //    follows the previous one on the same CU with no launch in between
-//    (measured at 8 x 1024 rows, 4096 x 14336: gate/up 1517 -> 1447 us).
+//    (measured at 8 x 1024 rows, 4096 x 14336: gate/up 1517 -> 1447 us);
+//  * an expert's rows are spread over its tiles in whole 16-row groups and
+//    each wave runs the K loop compiled for its number of live 16-row groups,
+//    so padding rows cost loads but almost no MFMAs; experts of more than
+//    eight tiles are walked in bands (map_tile_balanced), so the tiles running
+//    together on an XCD share their operand tiles in L2.
 #include <algorithm>
 #include <type_traits>
 
