@@ -1,6 +1,7 @@
 """Host logic of bench.py (CPU only): the one-GPU refusal, the algorithmic work
 per launch that the roofline divides by, the lookup of committed HBM-traffic
-records by kernel-source hash, and the kernel-name mapping.
+records by kernel-source hash (and that profiles/ holds records for the
+kernel sources as committed), and the kernel-name mapping.
 
 The weight sizes are pinned to the parameter counts of the layers the pages
 describe: E experts of three F x d matrices (gate, up, down), at the weight
@@ -116,3 +117,21 @@ def test_traffic_record_is_used_only_for_the_sources_it_was_taken_on(tmp_path, m
     assert bench.kernel_source_hash() == h
     (csrc / "k.h").write_text("#pragma once\n")
     assert bench.recorded_traffic("gemm_gate_up_bf16", "mixtral_bf16") is None
+
+
+# the workloads whose HBM traffic profiles/ records, and the weight type of each
+PROFILED = {"mixtral_bf16": "bf16", "gumbel_bf16": "bf16", "fine_shared_bf16": "bf16",
+            "fine_grouped_bf16": "bf16", "skewed_fp8": "fp8", "skewed_fp8_reroute": "fp8",
+            "skewed_fp8_decode": "fp8", "skewed_int4_decode": "int4"}
+
+
+@pytest.mark.parametrize("workload", sorted(PROFILED))
+def test_committed_traffic_records_describe_the_committed_kernels(workload):
+    """Every profiled workload has copy-calibrated FETCH/WRITE records of both expert
+    passes taken on exactly these kernel sources (a kernel edit without a new
+    profile leaves bench.py's `traffic` null, and this test names the workload)."""
+    wt = PROFILED[workload]
+    for kernel in (f"gemm_gate_up_{wt}", f"gemm_down_{wt}"):
+        rec = bench.recorded_traffic(kernel, workload)
+        assert rec is not None, f"profiles/ holds no traffic record of {kernel} at {workload} for these sources"
+        assert rec["bytes_per_launch"] > 0
