@@ -38,3 +38,22 @@ def test_fullsize_forward(name):
         assert np.all(f["out"][dropped_all] == 0.0)
     del inp, ora
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("name", ["mixtral_bf16", "fine_shared_bf16", "skewed_fp8_reroute"])
+def test_fullsize_forward_is_deterministic(name):
+    """Two calls at full size (a fresh workspace for the second) give the same bits:
+    no kernel lets the order of arrival decide an order of arithmetic -- the
+    stream-K parts are added in part order, the re-routing rounds settle one
+    stable assignment, the combine adds its slots in j order."""
+    assert torch.cuda.is_available()
+    sh = W.WORKLOADS[name]
+    G.banner(f"determinism {name} T={sh.T}")
+    inp = W.make_inputs(sh, device="cuda")
+    a = G.run_forward(inp)
+    b = G.run_forward(inp)
+    assert np.array_equal(a["out"], b["out"])
+    for key in ("topk_idx", "topk_w", "dest_row", "counts", "kept"):
+        assert np.array_equal(a[key], b[key]), key
+    del inp, a, b
+    torch.cuda.empty_cache()
