@@ -39,7 +39,12 @@ CASES = {
     "int4_tiles32": (W.DT_INT4, COUNTS_B),
     "bf16_big": (W.DT_BF16, COUNTS_C),
     "bf16_big_bands": (W.DT_BF16, COUNTS_D),
+    # the same experts with F = 4096: the down pass (44 tiles, 64 K steps) is cut
+    # into stream-K parts, so parts of banded tiles meet in the partial slots
+    "bf16_big_bands_sk": (W.DT_BF16, COUNTS_D),
 }
+# inner dim per case (256 unless named)
+F_OF = {"bf16_big_bands": 512, "bf16_big_bands_sk": 4096}
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -48,7 +53,7 @@ def test_expert_ffn_every_live_row_group(name):
     dev = torch.device("cuda")
     w_dtype, counts = CASES[name]
     R = int(sum(counts))
-    F = 512 if name == "bf16_big_bands" else 256  # (four gate/up n-tiles per band row)
+    F = F_OF.get(name, 256)
     sh = W.WORKLOADS["mixtral_bf16"].replace(name=f"rows_{name}", T=R, d=256, E=len(counts), k=1, F=F,
                                              w_dtype=w_dtype)
     G.banner(f"ffn rows {name} R={R} w={w_dtype}")
